@@ -1,0 +1,157 @@
+/* e2d2_attn.h -- C ABI of the MI355X (gfx950) attention hot path of E2D2, the
+ * encoder-decoder block diffusion language model.
+ *
+ * Pages cited, by title and section:
+ *   [Notes]   "Encoder-Decoder Diffusion Language Models for Efficient Training and
+ *             Inference", Paper-Notes page (zhaoyang97.github.io).
+ *   [Summary] ai.info "AI summary" page on the same paper.
+ *   [BD3]     "Block Diffusion: Interpolating Between Autoregressive and Diffusion
+ *             Language Models", xllm-io review.
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, row-major [B][H][N][d] with d contiguous and no padding;
+ *     query tensors have Hq heads, key/value tensors Hkv heads, Hq % Hkv == 0, and
+ *     query head hq reads key/value head hq / (Hq / Hkv).
+ *   - dtype E2D2_BF16: q, k, v and o are bfloat16; E2D2_F32: all float32.  LSE
+ *     outputs are always float32 [B][Hq][N_q], natural log of the sum of
+ *     exp(scale * q.k) over the allowed keys of the row.  Any LSE pointer may be NULL
+ *     (not written).
+ *   - Blocks hold S consecutive positions from position 0; the last block may be
+ *     shorter ([BD3] 三 技术架构, 块级分解).  blk(i) = floor(i / S).
+ *   - Every data pointer is a DEVICE pointer, except where noted.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the null stream).
+ *   - Every call validates its arguments on the host first and, on error, returns
+ *     the status WITHOUT launching anything or touching device memory.  On success
+ *     the work is enqueued on `stream` and the call returns at once; faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - The library allocates, frees and synchronises no device memory, keeps no
+ *     pointer after a call returns and holds no mutable global state; calls are
+ *     thread-safe.  The caller owns every buffer, including the KV cache and its
+ *     length.  Outputs must not alias inputs.
+ *   - Results are deterministic: identical inputs and arguments give bitwise
+ *     identical outputs (no floating-point atomics).
+ *   - dbg_tile_visits: optional device counter (unsigned long long).  When non-NULL
+ *     the kernels ADD the number of (batch, query head, query tile, key tile) tiles
+ *     they visited, a tile being visited when it holds at least one allowed
+ *     (query, key) pair; key tiles are laid out separately inside each key source.
+ *     Pass NULL when timing.
+ */
+#ifndef E2D2_ATTN_H
+#define E2D2_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define E2D2_ABI_VERSION 1
+
+typedef enum {
+  E2D2_OK = 0,
+  E2D2_ERR_NULL = 1,        /* a required pointer is NULL */
+  E2D2_ERR_SHAPE = 2,       /* a size is <= 0 (or < 0 where 0 is allowed), Hq % Hkv != 0,
+                               or a size exceeds the supported range */
+  E2D2_ERR_UNSUPPORTED = 3, /* the (dtype, d) pair or the kind is not built */
+  E2D2_ERR_CAPACITY = 4,    /* cache_len + S exceeds cache_cap */
+  E2D2_ERR_WORKSPACE = 5,   /* workspace smaller than e2d2_attn_denoise_workspace_bytes */
+  E2D2_ERR_HIP = 6          /* a HIP launch failed; see e2d2_last_hip_error */
+} e2d2_status;
+
+typedef enum { E2D2_F32 = 0, E2D2_BF16 = 1 } e2d2_dtype;
+
+typedef enum {
+  E2D2_KIND_ENC = 0,     /* encoder block-causal mask */
+  E2D2_KIND_DEC = 1,     /* decoder mask over [clean | noised] keys */
+  E2D2_KIND_DENOISE = 2  /* denoising step over [cache | own block] keys */
+} e2d2_kind;
+
+/* Version of this header's ABI (E2D2_ABI_VERSION). */
+int e2d2_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* e2d2_status_string(int status);
+
+/* hipError_t of the last call on this thread that returned E2D2_ERR_HIP (0 if none). */
+int e2d2_last_hip_error(void);
+
+/* Supported head dimensions: d in {32, 64, 128} for both dtypes. */
+
+/* Encoder block-causal attention over L clean tokens ([Notes] 方法详解 §4 训练算法:
+ * a clean token attends the tokens of its own block and of every earlier block).
+ * Row i attends keys j with blk(j) <= blk(i).
+ *   q [B][Hq][L][d]; k, v [B][Hkv][L][d]; o [B][Hq][L][d]; lse [B][Hq][L] or NULL.
+ *   scale multiplies q.k before the softmax (1/sqrt(d) usually). */
+e2d2_status e2d2_attn_encoder_blockcausal(int dtype, int B, int Hq, int Hkv, int L, int d,
+                                          int S, float scale, const void* q, const void* k,
+                                          const void* v, void* o, float* lse,
+                                          unsigned long long* dbg_tile_visits, void* stream);
+
+/* Training forward of the fused decoder self+cross attention ([Notes] §4 训练算法 and
+ * §2 两种连接方式): noised query i attends, under ONE softmax, the clean context keys
+ * j of strictly earlier blocks (blk(j) < blk(i)) and the noised keys j of its own
+ * block (blk(j) == blk(i)) -- 2L keys in all, ordered [clean | noised].
+ *   q_dec [B][Hq][L][d]; k_ctx, v_ctx, k_dec, v_dec [B][Hkv][L][d];
+ *   o_dec [B][Hq][L][d]; lse_dec [B][Hq][L] or NULL.
+ * k_ctx/v_ctx are the clean-context keys/values the decoder conditions on: the
+ * encoder's own K/V in the shared-KV-cache wiring, or the decoder's projection of
+ * the encoder output in the last-hidden-state wiring.
+ * Optional, same launch: when q_enc is non-NULL the encoder block-causal attention
+ * of (q_enc, k_ctx, v_ctx) is computed too, into o_enc [B][Hq][L][d] (required then)
+ * and lse_enc (may be NULL); pass q_enc = o_enc = lse_enc = NULL for the decoder only. */
+e2d2_status e2d2_attn_train_fwd(int dtype, int B, int Hq, int Hkv, int L, int d, int S,
+                                float scale, const void* q_dec, const void* k_ctx,
+                                const void* v_ctx, const void* k_dec, const void* v_dec,
+                                void* o_dec, float* lse_dec, const void* q_enc, void* o_enc,
+                                float* lse_enc, unsigned long long* dbg_tile_visits,
+                                void* stream);
+
+/* Bytes of device workspace e2d2_attn_denoise_step needs for these sizes (0 when the
+ * call needs none; a NULL workspace is then accepted).  Host-only, no GPU needed. */
+size_t e2d2_attn_denoise_workspace_bytes(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                         long long cache_len);
+
+/* One denoising step ([Notes] §3 采样算法; [Summary] "Methodology in Plain English"):
+ * the S queries of the current [MASK] block attend every cached clean key
+ * (rows [0, cache_len) of the cache) and every key of their own block, with no mask.
+ *   q_blk [B][Hq][S][d]; k_cache, v_cache [B][Hkv][cache_cap][d] (rows beyond
+ *   cache_len are not read); k_blk, v_blk [B][Hkv][S][d] this step's own-block K/V;
+ *   o_blk [B][Hq][S][d]; lse_blk [B][Hq][S] or NULL.
+ *   cache_len >= 0 (0 = empty cache) and cache_len <= cache_cap.
+ *   workspace: device scratch of at least e2d2_attn_denoise_workspace_bytes(...)
+ *   bytes, owned by the caller, contents ignored on entry; calls that share one
+ *   workspace must be ordered on one stream. */
+e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float scale,
+                                   const void* q_blk, const void* k_cache, const void* v_cache,
+                                   long long cache_len, long long cache_cap, const void* k_blk,
+                                   const void* v_blk, void* o_blk, float* lse_blk,
+                                   void* workspace, size_t workspace_bytes,
+                                   unsigned long long* dbg_tile_visits, void* stream);
+
+/* KV-cache append after a block is finished ([Notes] §3 采样算法: the finished block
+ * goes through the encoder, which updates the KV cache): copies k_new, v_new
+ * [B][Hkv][S][d] into rows [cache_len, cache_len + S) of k_cache, v_cache
+ * [B][Hkv][cache_cap][d].  Needs cache_len + S <= cache_cap (else
+ * E2D2_ERR_CAPACITY).  The caller then advances its cache length by S.  Bitwise copy. */
+e2d2_status e2d2_kv_cache_append(int dtype, int B, int Hkv, int S, int d, void* k_cache,
+                                 void* v_cache, long long cache_len, long long cache_cap,
+                                 const void* k_new, const void* v_new, void* stream);
+
+/* Query/key tile shape (bm query rows of one head, bn keys) the kernels use for a
+ * kind, dtype and head dimension.  Host-only; bm and bn are host pointers. */
+e2d2_status e2d2_attn_tile_shape(int kind, int dtype, int d, int* bm, int* bn);
+
+/* Tiles the block-sparse schedule visits (holding >= 1 allowed pair) and, of those,
+ * the full ones (every pair allowed), summed over B * Hq heads, for query tiles of
+ * bm rows and key tiles of bn keys laid out per key source.  ENC and DEC use L; DEC
+ * counts both of its sources; DENOISE uses S query rows and cache_len + S keys (L
+ * ignored).  Host-only; visited and full are host pointers. */
+e2d2_status e2d2_attn_count_tiles(int kind, int B, int Hq, int L, int S, long long cache_len,
+                                  int bm, int bn, unsigned long long* visited,
+                                  unsigned long long* full);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E2D2_ATTN_H */

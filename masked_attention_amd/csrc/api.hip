@@ -1,0 +1,348 @@
+// C-ABI entry points: argument validation (before anything touches the GPU), tile
+// schedule sizing and kernel dispatch.  Declarations and contracts: include/e2d2_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/e2d2_attn.h"
+#include "kernels.h"
+#include "schedule.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr long long kMaxLen = 1ll << 24;  // per-head rows (sequence, cache capacity)
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+e2d2_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return E2D2_OK;
+  g_last_hip_error = (int)e;
+  return E2D2_ERR_HIP;
+}
+
+// Shared shape checks of the training calls.
+e2d2_status check_train_shape(int dtype, int B, int Hq, int Hkv, int L, int d, int S,
+                              float scale) {
+  if (dtype != E2D2_F32 && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || S <= 0) return E2D2_ERR_SHAPE;
+  if (Hq % Hkv != 0 || L > kMaxLen || !scale_ok(scale)) return E2D2_ERR_SHAPE;
+  const int bm = dtype == E2D2_BF16 ? e2d2::train_tile_bm() : e2d2::kF32TileBM;
+  if ((long long)B * Hq * 2 * cdiv(L, bm) > INT32_MAX) return E2D2_ERR_SHAPE;
+  return E2D2_OK;
+}
+
+// Denoise query grouping: 32-row chunks per head and 2 column blocks per workgroup.
+struct DenoiseShape {
+  int g, nrc, ncb, n_qgroups, n_tiles_cache, n_tiles, n_split;
+};
+DenoiseShape denoise_shape(int B, int Hq, int Hkv, int S, long long C) {
+  DenoiseShape s;
+  s.g = Hq / Hkv;
+  s.nrc = cdiv(S, 32);
+  s.ncb = s.g * s.nrc;
+  s.n_qgroups = cdiv(s.ncb, 2);
+  s.n_tiles_cache = cdiv(C, e2d2::kDenoiseTileBN);
+  s.n_tiles = s.n_tiles_cache + cdiv(S, e2d2::kDenoiseTileBN);
+  s.n_split = e2d2::denoise_splits(B, Hkv, s.n_qgroups, s.n_tiles);
+  return s;
+}
+
+size_t denoise_ws_bytes(int dtype, int B, int Hq, int Hkv, int S, int d, long long C) {
+  if (dtype != E2D2_BF16) return 0;
+  const DenoiseShape s = denoise_shape(B, Hq, Hkv, S, C);
+  if (s.n_split == 1) return 0;
+  const size_t rows = (size_t)B * Hkv * s.n_qgroups * s.n_split * 64;
+  const size_t o_bytes = rows * d * sizeof(float);
+  const size_t ml_bytes = rows * 2 * sizeof(float);
+  return ((o_bytes + 255) & ~(size_t)255) + ml_bytes;
+}
+
+void fill_f32_common(e2d2::F32Params& p, int B, int Hq, int Hkv, int L, int S, long long C,
+                     float scale, unsigned long long* visits) {
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.L = L;
+  p.S = S;
+  p.C = (int)C;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  p.visits = visits;
+}
+
+}  // namespace
+
+extern "C" {
+
+int e2d2_abi_version(void) { return E2D2_ABI_VERSION; }
+
+const char* e2d2_status_string(int status) {
+  switch (status) {
+    case E2D2_OK: return "ok";
+    case E2D2_ERR_NULL: return "a required pointer is NULL";
+    case E2D2_ERR_SHAPE: return "invalid size, head grouping, scale or alignment";
+    case E2D2_ERR_UNSUPPORTED: return "unsupported dtype, head dimension or kind";
+    case E2D2_ERR_CAPACITY: return "cache_len + S exceeds cache_cap";
+    case E2D2_ERR_WORKSPACE: return "workspace too small";
+    case E2D2_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int e2d2_last_hip_error(void) { return g_last_hip_error; }
+
+e2d2_status e2d2_attn_encoder_blockcausal(int dtype, int B, int Hq, int Hkv, int L, int d, int S,
+                                          float scale, const void* q, const void* k,
+                                          const void* v, void* o, float* lse,
+                                          unsigned long long* dbg_tile_visits, void* stream) {
+  e2d2_status st = check_train_shape(dtype, B, Hq, Hkv, L, d, S, scale);
+  if (st != E2D2_OK) return st;
+  if (!q || !k || !v || !o) return E2D2_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned4(lse)) || (dbg_tile_visits && ((uintptr_t)dbg_tile_visits & 7u)))
+    return E2D2_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == E2D2_BF16) {
+    e2d2::TrainParams p = {};
+    p.q[0] = (const __bf16*)q;
+    p.o[0] = (__bf16*)o;
+    p.lse[0] = lse;
+    p.k[0] = p.k[1] = (const __bf16*)k;
+    p.v[0] = p.v[1] = (const __bf16*)v;
+    p.kinds[0] = p.kinds[1] = e2d2::kEnc;
+    p.n_kinds = 1;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
+    p.n_qtiles = cdiv(L, e2d2::train_tile_bm());
+    p.xcd_groups = (B * Hq) % 8 == 0;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    p.visits = dbg_tile_visits;
+    return hip_status(e2d2::launch_train_bf16(p, d, s));
+  }
+  e2d2::F32Params p = {};
+  fill_f32_common(p, B, Hq, Hkv, L, S, 0, scale, dbg_tile_visits);
+  p.q[0] = (const float*)q;
+  p.o[0] = (float*)o;
+  p.lse[0] = lse;
+  p.kf[0][0] = p.kf[0][1] = (const float*)k;
+  p.vf[0][0] = p.vf[0][1] = (const float*)v;
+  p.src_rows[0][0] = p.src_rows[0][1] = L;
+  p.kinds[0] = p.kinds[1] = e2d2::kEnc;
+  p.n_kinds = 1;
+  p.n_qtiles = cdiv(L, e2d2::kF32TileBM);
+  return hip_status(e2d2::launch_attn_f32(p, d, s));
+}
+
+e2d2_status e2d2_attn_train_fwd(int dtype, int B, int Hq, int Hkv, int L, int d, int S, float scale,
+                                const void* q_dec, const void* k_ctx, const void* v_ctx,
+                                const void* k_dec, const void* v_dec, void* o_dec, float* lse_dec,
+                                const void* q_enc, void* o_enc, float* lse_enc,
+                                unsigned long long* dbg_tile_visits, void* stream) {
+  e2d2_status st = check_train_shape(dtype, B, Hq, Hkv, L, d, S, scale);
+  if (st != E2D2_OK) return st;
+  if (!q_dec || !k_ctx || !v_ctx || !k_dec || !v_dec || !o_dec) return E2D2_ERR_NULL;
+  const bool with_enc = q_enc != nullptr;
+  if (with_enc && !o_enc) return E2D2_ERR_NULL;
+  if (!with_enc && (o_enc || lse_enc)) return E2D2_ERR_NULL;
+  if (!aligned16(q_dec) || !aligned16(k_ctx) || !aligned16(v_ctx) || !aligned16(k_dec) ||
+      !aligned16(v_dec) || !aligned16(o_dec) || (lse_dec && !aligned4(lse_dec)) ||
+      (with_enc && (!aligned16(q_enc) || !aligned16(o_enc) || (lse_enc && !aligned4(lse_enc)))) ||
+      (dbg_tile_visits && ((uintptr_t)dbg_tile_visits & 7u)))
+    return E2D2_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == E2D2_BF16) {
+    e2d2::TrainParams p = {};
+    p.q[0] = (const __bf16*)q_dec;
+    p.o[0] = (__bf16*)o_dec;
+    p.lse[0] = lse_dec;
+    p.q[1] = (const __bf16*)q_enc;
+    p.o[1] = (__bf16*)o_enc;
+    p.lse[1] = lse_enc;
+    p.k[0] = (const __bf16*)k_ctx;
+    p.v[0] = (const __bf16*)v_ctx;
+    p.k[1] = (const __bf16*)k_dec;
+    p.v[1] = (const __bf16*)v_dec;
+    p.kinds[0] = e2d2::kDec;
+    p.kinds[1] = e2d2::kEnc;
+    p.n_kinds = with_enc ? 2 : 1;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
+    p.n_qtiles = cdiv(L, e2d2::train_tile_bm());
+    p.xcd_groups = (B * Hq * p.n_kinds) % 8 == 0;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    p.visits = dbg_tile_visits;
+    return hip_status(e2d2::launch_train_bf16(p, d, s));
+  }
+  e2d2::F32Params p = {};
+  fill_f32_common(p, B, Hq, Hkv, L, S, 0, scale, dbg_tile_visits);
+  p.q[0] = (const float*)q_dec;
+  p.o[0] = (float*)o_dec;
+  p.lse[0] = lse_dec;
+  p.q[1] = (const float*)q_enc;
+  p.o[1] = (float*)o_enc;
+  p.lse[1] = lse_enc;
+  for (int sl = 0; sl < 2; ++sl) {
+    p.kf[sl][0] = (const float*)k_ctx;
+    p.vf[sl][0] = (const float*)v_ctx;
+    p.kf[sl][1] = (const float*)k_dec;
+    p.vf[sl][1] = (const float*)v_dec;
+    p.src_rows[sl][0] = p.src_rows[sl][1] = L;
+  }
+  p.kinds[0] = e2d2::kDec;
+  p.kinds[1] = e2d2::kEnc;
+  p.n_kinds = with_enc ? 2 : 1;
+  p.n_qtiles = cdiv(L, e2d2::kF32TileBM);
+  return hip_status(e2d2::launch_attn_f32(p, d, s));
+}
+
+size_t e2d2_attn_denoise_workspace_bytes(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                         long long cache_len) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || !head_dim_ok(d) || Hq % Hkv != 0 ||
+      cache_len < 0 || cache_len > kMaxLen)
+    return 0;
+  return denoise_ws_bytes(dtype, B, Hq, Hkv, S, d, cache_len);
+}
+
+e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float scale,
+                                   const void* q_blk, const void* k_cache, const void* v_cache,
+                                   long long cache_len, long long cache_cap, const void* k_blk,
+                                   const void* v_blk, void* o_blk, float* lse_blk, void* workspace,
+                                   size_t workspace_bytes, unsigned long long* dbg_tile_visits,
+                                   void* stream) {
+  if (dtype != E2D2_F32 && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Hq % Hkv != 0 || !scale_ok(scale))
+    return E2D2_ERR_SHAPE;
+  if (cache_len < 0 || cache_cap < 0 || cache_len > cache_cap || cache_cap > kMaxLen ||
+      S > kMaxLen)
+    return E2D2_ERR_SHAPE;
+  if (!q_blk || !k_blk || !v_blk || !o_blk) return E2D2_ERR_NULL;
+  if (cache_len > 0 && (!k_cache || !v_cache)) return E2D2_ERR_NULL;
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_blk) ||
+      (cache_len > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) ||
+      (lse_blk && !aligned4(lse_blk)) || (dbg_tile_visits && ((uintptr_t)dbg_tile_visits & 7u)))
+    return E2D2_ERR_SHAPE;
+  const size_t need = denoise_ws_bytes(dtype, B, Hq, Hkv, S, d, cache_len);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return E2D2_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  // An empty cache has no rows to read; any non-NULL pointer stands in.
+  const void* kc = cache_len > 0 ? k_cache : k_blk;
+  const void* vc = cache_len > 0 ? v_cache : v_blk;
+  if (dtype == E2D2_BF16) {
+    const DenoiseShape sh = denoise_shape(B, Hq, Hkv, S, cache_len);
+    if ((long long)B * Hkv * sh.n_qgroups * sh.n_split > INT32_MAX) return E2D2_ERR_SHAPE;
+    e2d2::DenoiseParams p = {};
+    p.q = (const __bf16*)q_blk;
+    p.k_cache = (const __bf16*)kc;
+    p.v_cache = (const __bf16*)vc;
+    p.k_blk = (const __bf16*)k_blk;
+    p.v_blk = (const __bf16*)v_blk;
+    p.o = (__bf16*)o_blk;
+    p.lse = lse_blk;
+    if (need > 0) {
+      const size_t rows = (size_t)B * Hkv * sh.n_qgroups * sh.n_split * 64;
+      p.ws_o = (float*)workspace;
+      p.ws_ml = (float*)((char*)workspace + ((rows * d * sizeof(float) + 255) & ~(size_t)255));
+    }
+    p.cap = cache_len > 0 ? cache_cap : 0;
+    p.C = (int)cache_len;
+    p.S = S;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.g = sh.g;
+    p.nrc = sh.nrc;
+    p.ncb = sh.ncb;
+    p.n_qgroups = sh.n_qgroups;
+    p.n_split = sh.n_split;
+    p.n_tiles = sh.n_tiles;
+    p.n_tiles_cache = sh.n_tiles_cache;
+    p.c = scale * 1.4426950408889634f;
+    p.visits = dbg_tile_visits;
+    return hip_status(e2d2::launch_denoise_bf16(p, d, s));
+  }
+  e2d2::F32Params p = {};
+  fill_f32_common(p, B, Hq, Hkv, 0, S, cache_len, scale, dbg_tile_visits);
+  p.q[0] = (const float*)q_blk;
+  p.o[0] = (float*)o_blk;
+  p.lse[0] = lse_blk;
+  p.kf[0][0] = (const float*)kc;
+  p.vf[0][0] = (const float*)vc;
+  p.src_rows[0][0] = cache_len > 0 ? (int)cache_cap : 0;
+  p.kf[0][1] = (const float*)k_blk;
+  p.vf[0][1] = (const float*)v_blk;
+  p.src_rows[0][1] = S;
+  p.kinds[0] = p.kinds[1] = e2d2::kDenoise;
+  p.n_kinds = 1;
+  p.n_qtiles = cdiv(S, e2d2::kF32TileBM);
+  if ((long long)B * Hq * p.n_qtiles > INT32_MAX) return E2D2_ERR_SHAPE;
+  return hip_status(e2d2::launch_attn_f32(p, d, s));
+}
+
+e2d2_status e2d2_kv_cache_append(int dtype, int B, int Hkv, int S, int d, void* k_cache,
+                                 void* v_cache, long long cache_len, long long cache_cap,
+                                 const void* k_new, const void* v_new, void* stream) {
+  if (dtype != E2D2_F32 && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
+  if (B <= 0 || Hkv <= 0 || S <= 0 || cache_len < 0 || cache_cap <= 0 || cache_cap > kMaxLen)
+    return E2D2_ERR_SHAPE;
+  if (cache_len + S > cache_cap) return E2D2_ERR_CAPACITY;
+  if (!k_cache || !v_cache || !k_new || !v_new) return E2D2_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return E2D2_ERR_SHAPE;
+  return hip_status(e2d2::launch_kv_append(dtype == E2D2_BF16 ? 2 : 4, B, Hkv, S, d, k_cache,
+                                           v_cache, cache_len, cache_cap, k_new, v_new,
+                                           (hipStream_t)stream));
+}
+
+e2d2_status e2d2_attn_tile_shape(int kind, int dtype, int d, int* bm, int* bn) {
+  if (!bm || !bn) return E2D2_ERR_NULL;
+  if ((dtype != E2D2_F32 && dtype != E2D2_BF16) || !head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
+  if (kind == E2D2_KIND_ENC || kind == E2D2_KIND_DEC) {
+    *bm = dtype == E2D2_BF16 ? e2d2::train_tile_bm() : e2d2::kF32TileBM;
+    *bn = dtype == E2D2_BF16 ? e2d2::train_tile_bn() : e2d2::kF32TileBN;
+    return E2D2_OK;
+  }
+  if (kind == E2D2_KIND_DENOISE) {
+    *bm = dtype == E2D2_BF16 ? e2d2::kDenoiseTileBM : e2d2::kF32TileBM;
+    *bn = dtype == E2D2_BF16 ? e2d2::kDenoiseTileBN : e2d2::kF32TileBN;
+    return E2D2_OK;
+  }
+  return E2D2_ERR_UNSUPPORTED;
+}
+
+e2d2_status e2d2_attn_count_tiles(int kind, int B, int Hq, int L, int S, long long cache_len,
+                                  int bm, int bn, unsigned long long* visited,
+                                  unsigned long long* full) {
+  if (!visited || !full) return E2D2_ERR_NULL;
+  if (kind != E2D2_KIND_ENC && kind != E2D2_KIND_DEC && kind != E2D2_KIND_DENOISE)
+    return E2D2_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || S <= 0 || bm <= 0 || bn <= 0 || S > kMaxLen) return E2D2_ERR_SHAPE;
+  if (kind != E2D2_KIND_DENOISE && (L <= 0 || L > kMaxLen)) return E2D2_ERR_SHAPE;
+  if (kind == E2D2_KIND_DENOISE && (cache_len < 0 || cache_len > kMaxLen)) return E2D2_ERR_SHAPE;
+  const int C = kind == E2D2_KIND_DENOISE ? (int)cache_len : 0;
+  const int Lm = kind == E2D2_KIND_DENOISE ? 0 : L;
+  const int Lq = e2d2::query_len(kind, Lm, S);
+  unsigned long long v = 0, f = 0;
+  for (int q0 = 0; q0 < Lq; q0 += bm) {
+    const int r1 = (q0 + bm < Lq ? q0 + bm : Lq) - 1;
+    for (int src = 0; src < e2d2::num_sources(kind); ++src) {
+      const e2d2::TileRange tr = e2d2::visited_tiles(kind, src, q0, r1, S, Lm, C, bn);
+      v += (unsigned long long)(tr.last - tr.first);
+      for (int t = tr.first; t < tr.last; ++t)
+        f += e2d2::tile_full(kind, src, q0, r1, S, Lm, C, bn, t) ? 1ull : 0ull;
+    }
+  }
+  *visited = v * (unsigned long long)B * Hq;
+  *full = f * (unsigned long long)B * Hq;
+  return E2D2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,381 @@
+// Training-forward attention of E2D2 on gfx950: encoder block-causal attention,
+// fused decoder self+cross attention over [clean | noised] keys, or both in one grid.
+//
+// Pages cited, by title and section:
+//   [Notes] "Encoder-Decoder Diffusion Language Models for Efficient Training and
+//           Inference", Paper-Notes page: 方法详解 §2 两种连接方式 (self- and
+//           cross-attention fused into one call), §4 训练算法 (the encoder mask and the
+//           decoder's 2L-key mask; the FLOPs table whose halved attention term is what
+//           skipping masked tiles realises).
+//
+// bf16 kernel, one workgroup = 4 waves = 128 query rows of one (batch, query head):
+//   * Each wave owns 32 query rows and keeps their Q fragments in registers.
+//   * The key axis is walked one 64-key tile at a time, source by source (clean
+//     context keys, then, for the decoder, the noised keys of the own blocks), over
+//     exactly the tiles that hold an allowed pair (schedule.h).  K and V tiles are
+//     loaded straight from HBM into a double-buffered, swizzled LDS tile with
+//     global_load_lds_dwordx4 while the previous tile is being computed.
+//   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so a
+//     lane holds 16 keys of ONE query row: the row max is an in-lane reduction plus one
+//     exchange with lane l^32, and the row sum needs no exchange until the end.
+//   * Online softmax in base 2 with the scale folded in (p = 2^(s*c - m*c), c =
+//     scale*log2 e), p rounded to bf16, then O^T += V^T P^T on the MFMA with V^T read
+//     by the transposing LDS read; fp32 accumulation throughout.
+//   * Within a tile, each wave classifies its 32x32 key blocks: empty blocks are
+//     skipped (no MFMA), full blocks skip the mask, the rest mask per element.
+//   * Epilogue: O = O^T / l in bf16, LSE = scale * m + ln l in fp32.
+//   * Work order: query tiles are issued from the last (most keys) to the first;
+//     when the number of (head, kind) items per tile level is a multiple of 8, each of
+//     the 8 XCDs gets a fixed contiguous set of heads so that a head's K/V tiles stay
+//     in one XCD's L2, and the encoder and decoder items of a head run side by side.
+#include "device_common.h"
+#include "kernels.h"
+#include "schedule.h"
+
+namespace e2d2 {
+namespace {
+
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(256) void train_fwd_bf16_kernel(TrainParams p) {
+  constexpr int NC = D / 16;   // MFMA k-steps over the head dim for S^T
+  constexpr int NDB = D / 32;  // 32-wide head-dim blocks of O^T
+  constexpr int TILE = kBN * D;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  __bf16 E2D2_LDS* lds = (__bf16 E2D2_LDS*)smem_raw;  // [2 buffers][K, V][TILE]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+
+  // ---- work item
+  const int BH = p.B * p.Hq;
+  const int per_level = BH * p.n_kinds;
+  const int w = blockIdx.x;
+  int level, rem;
+  if (p.xcd_groups) {
+    const int per_xcd = per_level >> 3;
+    const int local = w >> 3;
+    level = local / per_xcd;
+    rem = (w & 7) * per_xcd + local % per_xcd;
+  } else {
+    level = w / per_level;
+    rem = w % per_level;
+  }
+  const int slot = rem % p.n_kinds;
+  const int bh = rem / p.n_kinds;
+  const int qtile = p.n_qtiles - 1 - level;
+  const int kind = p.kinds[slot];
+  const int b = bh / p.Hq;
+  const int hq = bh % p.Hq;
+  const int hk = hq / (p.Hq / p.Hkv);
+  const int L = p.L, S = p.S;
+
+  const int q0 = qtile * kBM;
+  const int r_last = min(q0 + kBM, L) - 1;
+  const int nsrc = num_sources(kind);
+  const TileRange tr0 = visited_tiles(kind, 0, q0, r_last, S, L, 0, kBN);
+  const TileRange tr1 = nsrc > 1 ? visited_tiles(kind, 1, q0, r_last, S, L, 0, kBN) : TileRange{0, 0};
+  const int n0 = tr0.last - tr0.first;
+  const int ntot = n0 + (tr1.last - tr1.first);
+
+  const size_t kv_off = ((size_t)b * p.Hkv + hk) * (size_t)L * D;
+  const __bf16* kbase[2] = {p.k[0] + kv_off, p.k[1] + kv_off};
+  const __bf16* vbase[2] = {p.v[0] + kv_off, p.v[1] + kv_off};
+
+  auto issue = [&](int t, int buf) {
+    const int src = t < n0 ? 0 : 1;
+    const int c = src == 0 ? tr0.first + t : tr1.first + (t - n0);
+    __bf16 E2D2_LDS* kt = lds + (2 * buf) * TILE;
+    __bf16 E2D2_LDS* vt = kt + TILE;
+    load_tile_lds<D, kBN>(kbase[src], c * kBN, L, kt, wave, kWaves, lane);
+    load_tile_lds<D, kBN>(vbase[src], c * kBN, L, vt, wave, kWaves, lane);
+  };
+
+  if (ntot > 0) issue(0, 0);
+
+  // ---- per-wave rows and per-lane query row
+  const int wq0 = q0 + wave * 32;
+  const bool wave_live = wq0 < L;
+  const int wr1 = min(wq0 + 32, L) - 1;
+  const int qi = wq0 + (lane & 31);
+  const bool row_ok = qi < L;
+  Interval iv[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    iv[s] = row_interval(kind, s, row_ok ? qi : 0, S, L, 0);
+    if (!row_ok) iv[s] = Interval{0, 0};
+  }
+
+  const size_t q_off = ((size_t)b * p.Hq + hq) * (size_t)L * D;
+  bf16x8 qf[NC];
+  {
+    const __bf16* qrow = p.q[slot] + q_off + (size_t)(row_ok ? qi : 0) * D + ((lane >> 5) << 3);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      bf16x8 v = *(const bf16x8*)(qrow + cc * 16);
+      if (!row_ok) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (__bf16)0.f;
+      }
+      qf[cc] = v;
+    }
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = zero16();
+  float m = -INFINITY;  // running max of raw scores q.k
+  float l = 0.f;        // lane-partial running sum
+  const float c = p.c;
+
+  for (int t = 0; t < ntot; ++t) {
+    const int buf = t & 1;
+    wait_vmem_all();
+    __syncthreads();  // tile t is in LDS for every wave; buffer buf^1 is free
+    if (t + 1 < ntot) issue(t + 1, buf ^ 1);
+
+    const int src = t < n0 ? 0 : 1;
+    const int ct = src == 0 ? tr0.first + t : tr1.first + (t - n0);
+    const __bf16 E2D2_LDS* kt = lds + (2 * buf) * TILE;
+    const __bf16 E2D2_LDS* vt = kt + TILE;
+    if (!wave_live) continue;
+
+    f32x16 sc[2];
+    int cls[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int k0 = ct * kBN + kb * 32;
+      const int k1 = min(k0 + 32, L);
+      int cl = classify(kind, src, wq0, wr1, S, L, 0, k0, k1);
+      if (cl == 2 && k1 - k0 < 32) cl = 1;
+      cls[kb] = cl;
+      if (cl) {
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+          acc = mfma32(read_k_frag<D>(kt, kb * 32, cc * 16, lane), qf[cc], acc);
+        if (cl == 1) {
+          const int kr = k0 + ((lane >> 5) << 2);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = kr + ((j >> 2) << 3) + (j & 3);
+            if (key < iv[src].lo || key >= iv[src].hi) acc[j] = -INFINITY;
+          }
+        }
+        sc[kb] = acc;
+      }
+    }
+    if (!cls[0] && !cls[1]) continue;
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (cls[kb]) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float base = m_new == -INFINITY ? 0.f : m_new * c;
+    const float alpha = fast_exp2(m * c - base);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (cls[kb]) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float e = fast_exp2(fmaf(sc[kb][j], c, -base));
+          sc[kb][j] = e;
+          rs += e;
+        }
+      }
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (cls[kb]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j0 = h * 8;
+          const bf16x8 pb = to_bf16x8(sc[kb][j0], sc[kb][j0 + 1], sc[kb][j0 + 2], sc[kb][j0 + 3],
+                                      sc[kb][j0 + 4], sc[kb][j0 + 5], sc[kb][j0 + 6],
+                                      sc[kb][j0 + 7]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            o[db] = mfma32(read_vt_frag<D>(vt, kb * 32 + h * 16, db * 32, lane), pb, o[db]);
+        }
+      }
+  }
+
+  // ---- epilogue
+  const float l_tot = l + __shfl_xor(l, 32);
+  if (row_ok) {
+    const float inv = 1.f / l_tot;
+    __bf16* orow = p.o[slot] + q_off + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = db * 32 + jg * 8 + ((lane >> 5) << 2);
+        bf16x4 v;
+        v[0] = (__bf16)(o[db][jg * 4 + 0] * inv);
+        v[1] = (__bf16)(o[db][jg * 4 + 1] * inv);
+        v[2] = (__bf16)(o[db][jg * 4 + 2] * inv);
+        v[3] = (__bf16)(o[db][jg * 4 + 3] * inv);
+        *(bf16x4*)(orow + d) = v;
+      }
+    if (p.lse[slot] != nullptr && lane < 32)
+      p.lse[slot][((size_t)b * p.Hq + hq) * L + qi] = m * p.scale + logf(l_tot);
+  }
+  if (p.visits != nullptr && threadIdx.x == 0) atomicAdd(p.visits, (unsigned long long)ntot);
+}
+
+// ---------------------------------------------------------------------------------
+// fp32 path: one wave per 64 query rows (one row per lane), 64-key fp32 tiles in LDS,
+// scores and P*V on the vector ALU in fp32, exp in fp32.  Serves every kind with two
+// key sources described by (pointer, allocated rows, length) per source.
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
+  constexpr int BN = 64;
+  __shared__ float ks[BN][D];  // every lane reads the same key row: broadcast, no padding
+  __shared__ float vs[BN][D];
+  const int lane = threadIdx.x;
+
+  const int per_level = p.B * p.Hq * p.n_kinds;
+  const int level = blockIdx.x / per_level;
+  const int rem = blockIdx.x % per_level;
+  const int slot = rem % p.n_kinds;
+  const int bh = rem / p.n_kinds;
+  const int qtile = p.n_qtiles - 1 - level;
+  const int kind = p.kinds[slot];
+  const int b = bh / p.Hq, hq = bh % p.Hq, hk = hq / (p.Hq / p.Hkv);
+  const int L = p.L, S = p.S, C = p.C;
+  const int Lq = query_len(kind, L, S);
+  const int q0 = qtile * 64;
+  if (q0 >= Lq) return;
+  const int r_last = min(q0 + 64, Lq) - 1;
+  const int qi = q0 + lane;
+  const bool row_ok = qi < Lq;
+
+  float q[D];
+  const float* qrow = p.q[slot] + (((size_t)b * p.Hq + hq) * Lq + (row_ok ? qi : 0)) * D;
+#pragma unroll
+  for (int j = 0; j < D; ++j) q[j] = row_ok ? qrow[j] : 0.f;
+  float o[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) o[j] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const float c = p.c;
+  int visits = 0;
+
+  for (int src = 0; src < num_sources(kind); ++src) {
+    const int n = source_len(kind, src, L, S, C);
+    const TileRange tr = visited_tiles(kind, src, q0, r_last, S, L, C, BN);
+    Interval iv = row_interval(kind, src, row_ok ? qi : 0, S, L, C);
+    if (!row_ok) iv = Interval{0, 0};
+    const int nalloc = p.src_rows[slot][src];
+    const float* kb = p.kf[slot][src] + ((size_t)b * p.Hkv + hk) * (size_t)nalloc * D;
+    const float* vb = p.vf[slot][src] + ((size_t)b * p.Hkv + hk) * (size_t)nalloc * D;
+    for (int t = tr.first; t < tr.last; ++t) {
+      ++visits;
+      __syncthreads();
+      for (int e = lane; e < BN * D; e += 64) {
+        const int r = e / D, col = e % D;
+        const int g = min(t * BN + r, n - 1);
+        ks[r][col] = kb[(size_t)g * D + col];
+        vs[r][col] = vb[(size_t)g * D + col];
+      }
+      __syncthreads();
+      for (int sub = 0; sub < BN; sub += 16) {
+        float s[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * BN + sub + r;
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < D; ++j) acc = fmaf(q[j], ks[sub + r][j], acc);
+          s[r] = (key >= iv.lo && key < iv.hi) ? acc : -INFINITY;
+          mx = fmaxf(mx, s[r]);
+        }
+        const float m_new = fmaxf(m, mx);
+        const float base = m_new == -INFINITY ? 0.f : m_new * c;
+        const float alpha = exp2f(m * c - base);
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < D; ++j) o[j] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2f(fmaf(s[r], c, -base));
+          l += e;
+#pragma unroll
+          for (int j = 0; j < D; ++j) o[j] = fmaf(e, vs[sub + r][j], o[j]);
+        }
+        m = m_new;
+      }
+    }
+  }
+  if (row_ok) {
+    float* orow = p.o[slot] + (((size_t)b * p.Hq + hq) * Lq + qi) * D;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int j = 0; j < D; ++j) orow[j] = o[j] * inv;
+    if (p.lse[slot] != nullptr) p.lse[slot][((size_t)b * p.Hq + hq) * Lq + qi] = m * p.scale + logf(l);
+  }
+  if (p.visits != nullptr && lane == 0) atomicAdd(p.visits, (unsigned long long)visits);
+}
+
+template <int D>
+hipError_t launch_train_bf16_d(const TrainParams& p, int grid, hipStream_t stream) {
+  const size_t smem = (size_t)2 * 2 * kBN * D * sizeof(__bf16);
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)train_fwd_bf16_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(train_fwd_bf16_kernel<D>, dim3(grid), dim3(256), smem, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_d(const F32Params& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(grid), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int train_tile_bm() { return kBM; }
+int train_tile_bn() { return kBN; }
+
+hipError_t launch_train_bf16(const TrainParams& p, int d, hipStream_t stream) {
+  const int grid = p.n_qtiles * p.B * p.Hq * p.n_kinds;
+  if (grid == 0) return hipSuccess;
+  switch (d) {
+    case 32: return launch_train_bf16_d<32>(p, grid, stream);
+    case 64: return launch_train_bf16_d<64>(p, grid, stream);
+    case 128: return launch_train_bf16_d<128>(p, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_f32(const F32Params& p, int d, hipStream_t stream) {
+  const int grid = p.n_qtiles * p.B * p.Hq * p.n_kinds;
+  if (grid == 0) return hipSuccess;
+  switch (d) {
+    case 32: return launch_f32_d<32>(p, grid, stream);
+    case 64: return launch_f32_d<64>(p, grid, stream);
+    case 128: return launch_f32_d<128>(p, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace e2d2

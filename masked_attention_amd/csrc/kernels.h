@@ -1,0 +1,85 @@
+// Launch parameters and launchers of the HIP kernels behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace e2d2 {
+
+// Training forward, bf16.  Grid item = (query tile, batch, query head, kind slot).
+// Slot s computes kind kinds[s] with queries q[s] into o[s], lse[s].  Key source 0 is
+// (k[0], v[0]) (clean keys), source 1 is (k[1], v[1]) (noised keys, decoder only).
+struct TrainParams {
+  const __bf16* q[2];
+  __bf16* o[2];
+  float* lse[2];
+  const __bf16* k[2];
+  const __bf16* v[2];
+  int kinds[2];
+  int n_kinds;
+  int B, Hq, Hkv, L, S;
+  int n_qtiles;
+  int xcd_groups;  // 1: (B*Hq*n_kinds) % 8 == 0, heads grouped per XCD
+  float scale;     // softmax scale
+  float c;         // scale * log2(e)
+  unsigned long long* visits;
+};
+
+// fp32 path for every kind.  Source `src` of slot `s` is kf[s][src], vf[s][src] with
+// src_rows[s][src] rows allocated per (batch, kv head).
+struct F32Params {
+  const float* q[2];
+  float* o[2];
+  float* lse[2];
+  const float* kf[2][2];
+  const float* vf[2][2];
+  int src_rows[2][2];
+  int kinds[2];
+  int n_kinds;
+  int B, Hq, Hkv, L, S, C;
+  int n_qtiles;
+  float scale, c;
+  unsigned long long* visits;
+};
+
+// Denoising step, bf16.  Grid item = (batch, kv head, query group, split).
+struct DenoiseParams {
+  const __bf16* q;
+  const __bf16* k_cache;
+  const __bf16* v_cache;
+  const __bf16* k_blk;
+  const __bf16* v_blk;
+  __bf16* o;
+  float* lse;
+  float* ws_o;   // [units][n_split][64][d] unnormalised partial O (n_split > 1)
+  float* ws_ml;  // [units][n_split][64][2] partial (max, sum) in base-2 units
+  long long cap;
+  int C, S, B, Hq, Hkv;
+  int g;          // query heads per kv head
+  int nrc;        // 32-row chunks per head: ceil(S / 32)
+  int ncb;        // column blocks per kv head: g * nrc
+  int n_qgroups;  // ceil(ncb / 2)
+  int n_split;
+  int n_tiles;    // key tiles of 32: ceil(C/32) + ceil(S/32)
+  int n_tiles_cache;
+  float c;        // scale * log2(e)
+  unsigned long long* visits;
+};
+
+int train_tile_bm();
+int train_tile_bn();
+constexpr int kF32TileBM = 64;
+constexpr int kF32TileBN = 64;
+constexpr int kDenoiseTileBM = 32;
+constexpr int kDenoiseTileBN = 32;
+
+hipError_t launch_train_bf16(const TrainParams& p, int d, hipStream_t stream);
+hipError_t launch_attn_f32(const F32Params& p, int d, hipStream_t stream);
+hipError_t launch_denoise_bf16(const DenoiseParams& p, int d, hipStream_t stream);
+// Denoise split sizing shared by the workspace query and the launch.
+int denoise_splits(int B, int Hkv, int n_qgroups, int n_tiles);
+hipError_t launch_kv_append(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
+                            void* v_cache, long long cache_len, long long cap,
+                            const void* k_new, const void* v_new, hipStream_t stream);
+
+}  // namespace e2d2
