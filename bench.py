@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the E2D2 attention hot path on one MI355X.
+
+Headline (``value``): useful TFLOP/s of the training attention forward -- encoder
+block-causal attention and fused decoder attention over [clean | noised] keys in ONE
+launch -- at B=8, 16 heads, d_head 64, L=1024, block S=16, bf16, N(0,1) synthetic
+inputs resident in HBM.  One step = one such launch.  Useful FLOPs = 4 * d * (allowed
+pairs of both masks) * B * H: the attention term of the FLOPs table, (L^2 + L S)/2
+pairs per mask ("Encoder-Decoder Diffusion Language Models for Efficient Training and
+Inference", Paper-Notes page, 方法详解 §4 训练算法).
+
+Also measured in the same run and reported in the same JSON line:
+  * ``denoise``: the inference step at B=32, 16 query / 8 KV heads, d_head 128, cache
+    2048, block S=32: 32 denoising steps with fresh block tensors, then the KV-cache
+    append; microseconds per step and algorithmic GB/s, with the Infinity Cache warm
+    (steady state) and flushed before every step (cold);
+  * ``long_train``: the same training forward at B=2, 16/8 heads, d_head 128, L=8192,
+    S=64, with LSE (MFMA-bound);
+  * ``roofline``: the training kernel's useful TFLOP/s against the bf16 MFMA peak,
+    with the kernel's average duration from HIP events on its stream;
+  * ``cpu_baseline``: the fp64 CPU oracle timed on the host cores on a bounded sample
+    of the training workload.
+
+``python bench.py --gpus N --steps K --warmup W``; this build runs on one GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "train_fwd_traffic.json")
+KERNEL_SOURCES = ["masked_attention_amd/csrc/attn_train.hip",
+                  "masked_attention_amd/csrc/device_common.h",
+                  "masked_attention_amd/csrc/schedule.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pairs_blockcausal(L: int, S: int) -> int:
+    """Allowed pairs of one mask (encoder or decoder) per head, counted block by block:
+    a row of block b sees (b+1) * S keys (clipped at L) in the encoder and, equally,
+    b * S earlier clean keys plus its own block in the decoder."""
+    total = 0
+    for start in range(0, L, S):
+        end = min(L, start + S)
+        total += (end - start) * end
+    return total
+
+
+def timed_launches(fn, n, stream):
+    """Run fn() n times with HIP events around every launch on ``stream``; returns
+    (total ms from the first start to the last end, mean per-launch ms)."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = [starts[i].elapsed_time(ends[i]) for i in range(n)]
+    return starts[0].elapsed_time(ends[-1]), sum(per) / n
+
+
+def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True):
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+
+    def fill(kind, H):
+        t = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=dev)
+        device_fill(t, seed, tensor_id(kind))
+        return t
+
+    qd, qe = fill(K.Q_DEC, Hq), fill(K.Q_ENC, Hq)
+    kc, vc, kd, vd = (fill(k, Hkv) for k in (K.K_CTX, K.V_CTX, K.K_DEC, K.V_DEC))
+    od, oe = torch.empty_like(qd), torch.empty_like(qe)
+    ld = torch.empty((B, Hq, L), device=dev) if with_lse else None
+    le = torch.empty((B, Hq, L), device=dev) if with_lse else None
+
+    def step():
+        m.e2d2_attn_train_fwd(qd, kc, vc, kd, vd, od, S, lse_dec=ld, q_enc=qe, o_enc=oe,
+                              lse_enc=le)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    total_ms, kern_ms = timed_launches(step, steps, stream)
+    wall = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    useful = 4.0 * d * 2 * pairs_blockcausal(L, S) * B * Hq
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=kern_ms,
+                useful_flop=useful, wall_s=wall)
+
+
+def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, C, S, T = 32, 16, 8, 128, 2048, 32, steps_per_block
+    cap = C + S
+
+    def fill(shape, kind, **kw):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        device_fill(t, seed, tensor_id(kind, **kw))
+        return t
+
+    kc = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    device_fill(kc, seed, tensor_id(K.K_CACHE), rows=C)
+    device_fill(vc, seed, tensor_id(K.V_CACHE), rows=C)
+    qs = [fill((B, Hq, S, d), K.Q_BLK, step=t) for t in range(T)]
+    ks = [fill((B, Hkv, S, d), K.K_BLK, step=t) for t in range(T)]
+    vs = [fill((B, Hkv, S, d), K.V_BLK, step=t) for t in range(T)]
+    kn, vn = fill((B, Hkv, S, d), K.K_NEW), fill((B, Hkv, S, d), K.V_NEW)
+    o = torch.empty((B, Hq, S, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, S), device=dev)
+    nws = m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, Hq, Hkv, S, d, C)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        m.e2d2_attn_denoise_step(qs[t], kc, vc, C, ks[t], vs[t], o, lse_blk=lse, workspace=ws)
+
+    def append():
+        m.e2d2_kv_cache_append(kc, vc, C, kn, vn)
+
+    for _ in range(warm_blocks):
+        for t in range(T):
+            step(t)
+        append()
+    torch.cuda.synchronize()
+    step_ms, append_ms = [], []
+    for _ in range(blocks):
+        for t in range(T):
+            _, ms = timed_launches(lambda: step(t), 1, stream)
+            step_ms.append(ms)
+        _, ms = timed_launches(append, 1, stream)
+        append_ms.append(ms)
+    # cold: flush the 256 MB Infinity Cache (and L2) with a 1 GiB write before each step
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold_ms = []
+    for t in range(min(T, 16)):
+        flush.zero_()
+        _, ms = timed_launches(lambda: step(t), 1, stream)
+        cold_ms.append(ms)
+    del flush
+    cache_bytes = 2 * B * Hkv * C * d * 2
+    blk_bytes = 2 * B * Hkv * S * d * 2
+    q_bytes = B * Hq * S * d * 2
+    o_bytes = B * Hq * S * d * 2 + B * Hq * S * 4
+    alg = cache_bytes + blk_bytes + q_bytes + o_bytes
+    warm = sorted(step_ms)[len(step_ms) // 2]
+    cold = sorted(cold_ms)[len(cold_ms) // 2]
+    app = sorted(append_ms)[len(append_ms) // 2]
+    app_bytes = 2 * 2 * B * Hkv * S * d * 2
+    return dict(
+        workload="denoise step, B32 Hq16 Hkv8 d128 cache 2048 block 32, bf16; 32 steps then append",
+        us_per_step_warm=warm * 1e3, us_per_step_cold=cold * 1e3,
+        us_per_step_mean_warm=sum(step_ms) / len(step_ms) * 1e3,
+        gbs_warm=alg / (warm * 1e-3) / 1e9, gbs_cold=alg / (cold * 1e-3) / 1e9,
+        algorithmic_bytes_per_step=alg, steps_timed=len(step_ms),
+        append_us=app * 1e3, append_gbs=app_bytes / (app * 1e-3) / 1e9,
+        roofline=dict(bound="hbm", achieved=round(alg / (cold * 1e-3) / 1e9, 1),
+                      peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(alg / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      note="cold (Infinity Cache flushed); warm figure in gbs_warm"),
+    )
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """fp64 oracle on a bounded sample of the training workload (whole heads, encoder
+    and decoder), in useful TFLOP/s like the GPU figure."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from synth import TensorKind as K, host_tensor, tensor_id
+
+    B, H, L, S, d, seed = 8, 16, 1024, 16, 64, 0xE2D20002
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    t_total = 0.0
+    done = 0
+    for b, h in heads:
+        def g(kind):
+            return host_tensor(seed, tensor_id(kind), (1, 1, L, d), "bf16", b0=b, h0=h)
+
+        qd, qe, kc, vc, kd, vd = (g(k) for k in (K.Q_DEC, K.Q_ENC, K.K_CTX, K.V_CTX, K.K_DEC,
+                                                  K.V_DEC))
+        t0 = time.perf_counter()
+        oracle.train_fwd(qd, kc, vc, kd, vd, S, 1.0 / math.sqrt(d), q_enc=qe)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    useful = 4.0 * d * 2 * pairs_blockcausal(L, S) * done
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return dict(value=useful / t_total / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{done} of {B * H} (batch, head) pairs of the B8 H16 d64 L1024 S16 "
+                       f"training forward, encoder + decoder, fp64 explicit-mask oracle, "
+                       f"{t_total:.1f} s; cores = BLAS threads (exp and masking run on one)",
+                seconds=round(t_total, 2), host_cpus=os.cpu_count())
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["all", "train", "denoise", "long", "copycal"],
+                    default="all",
+                    help="restrict the run (profiling); 'copycal' runs only a plain 1 GiB "
+                         "device copy, the reference for scaling HBM byte counters")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import masked_attention_amd as m
+
+    m.lib()  # fail loudly when the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    out = {}
+    train = None
+    if args.only == "copycal":
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copycal_bytes_read": n, "copycal_bytes_written": n, "launches": 3}))
+        return
+    if args.only in ("all", "train"):
+        B, H, L, S, d = 8, 16, 1024, 16, 64
+        train = bench_train(B, H, H, L, S, d, args.steps, args.warmup, 0xE2D20002)
+        print(f"[bench] train fwd B{B} H{H} d{d} L{L} S{S}: {train['ms_per_step'] * 1e3:.1f} us/step, "
+              f"kernel {train['kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+    if args.only in ("all", "long"):
+        lt = bench_train(2, 16, 8, 8192, 64, 128, max(3, args.steps // 10), 2, 0xE2D20004)
+        out["long_train"] = dict(
+            workload="training fwd enc+dec, B2 Hq16 Hkv8 d128 L8192 S64, bf16, with LSE",
+            ms_per_step=round(lt["ms_per_step"], 4),
+            tflops=round(lt["useful_flop"] / (lt["kernel_ms"] * 1e-3) / 1e12, 1),
+            frac_of_peak=round(lt["useful_flop"] / (lt["kernel_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+        print(f"[bench] long train: {lt['kernel_ms']:.3f} ms, {out['long_train']['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+    if args.only in ("all", "denoise"):
+        out["denoise"] = bench_denoise(32, 4, 1, 0xE2D20003)
+        print(f"[bench] denoise: warm {out['denoise']['us_per_step_warm']:.1f} us "
+              f"({out['denoise']['gbs_warm']:.0f} GB/s), cold {out['denoise']['us_per_step_cold']:.1f} us "
+              f"({out['denoise']['gbs_cold']:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    if train is None:
+        print(json.dumps(out))
+        return
+    value = train["useful_flop"] / (train["ms_per_step"] * 1e-3) / 1e12
+    achieved = train["useful_flop"] / (train["kernel_ms"] * 1e-3) / 1e12
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    line = {
+        "metric": "useful TFLOP/s (masked attn fwd, % MFMA peak); denoise-step us + HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(train["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "E2D2 training attention fwd, encoder block-causal + decoder "
+                               "2L-key mask in one launch, B8 H16 d64 L1024 S16 bf16, "
+                               "N(0,1) inputs", "global_batch": 8, "seq_len": 1024,
+                   "block": 16, "heads": 16, "d_head": 64, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "train_fwd_bf16_kernel<64>",
+                     "kernel_us": round(train["kernel_ms"] * 1e3, 2),
+                     "useful_flop_per_launch": train["useful_flop"]},
+    }
+    line.update(out)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
