@@ -17,6 +17,9 @@ bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+// One (batch, head) slice of `rows` rows is addressed with 32-bit byte offsets (buffer
+// resources) on the GPU: keep it below 2 GiB.
+bool slice_ok(long long rows, int d) { return rows * d * 2 < (1ll << 31); }
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 e2d2_status hip_status(hipError_t e) {
@@ -32,6 +35,7 @@ e2d2_status check_train_shape(int dtype, int B, int Hq, int Hkv, int L, int d, i
   if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || S <= 0) return E2D2_ERR_SHAPE;
   if (Hq % Hkv != 0 || L > kMaxLen || !scale_ok(scale)) return E2D2_ERR_SHAPE;
+  if (!slice_ok(L, d)) return E2D2_ERR_SHAPE;
   const int bm = dtype == E2D2_BF16 ? e2d2::train_tile_bm() : e2d2::kF32TileBM;
   if ((long long)B * Hq * 2 * cdiv(L, bm) > INT32_MAX) return E2D2_ERR_SHAPE;
   return E2D2_OK;
@@ -220,7 +224,7 @@ e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Hq % Hkv != 0 || !scale_ok(scale))
     return E2D2_ERR_SHAPE;
   if (cache_len < 0 || cache_cap < 0 || cache_len > cache_cap || cache_cap > kMaxLen ||
-      S > kMaxLen)
+      S > kMaxLen || !slice_ok(cache_cap, d) || !slice_ok(S, d))
     return E2D2_ERR_SHAPE;
   if (!q_blk || !k_blk || !v_blk || !o_blk) return E2D2_ERR_NULL;
   if (cache_len > 0 && (!k_cache || !v_cache)) return E2D2_ERR_NULL;

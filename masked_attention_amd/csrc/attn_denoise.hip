@@ -18,10 +18,11 @@
 //   * The key axis (cache rows [0, C), then the block's own S keys) is cut into
 //     32-key tiles.  The 4 waves of a workgroup take every 4th tile and stream them
 //     independently (no barrier in the loop) through a wave-private, double-buffered
-//     LDS stage filled by global_load_lds_dwordx4, so each wave keeps one tile in
+//     LDS stage filled by buffer_load_dwordx4 ... lds, so each wave keeps one tile in
 //     flight while it computes the other.
 //   * Per tile: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with an
-//     online base-2 softmax, as in the training kernel; only ragged tile ends mask.
+//     online base-2 softmax with lazy rescaling, as in the training kernel; only
+//     ragged tile ends mask.
 //   * The 4 waves' partial (max, sum, O) are merged in LDS, in a fixed order.  When
 //     there are too few (batch, kv head) items to fill the GPU, the key axis is also
 //     split over workgroups; each split writes its partial to the workspace and a
@@ -38,10 +39,6 @@ constexpr int kTN = 32;     // keys per tile
 constexpr int kNQB = 2;     // column blocks (32 query rows each) per workgroup
 constexpr int kWaves = 4;
 
-// s_waitcnt vmcnt(n) immediate for gfx9 (vmcnt split over bits 3:0 and 15:14;
-// expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
 template <int D>
 __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
   constexpr int NC = D / 16;
@@ -49,7 +46,6 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
   constexpr int TILE = kTN * D;            // elements of one K or V tile
   constexpr int NI = kTN * (D / 8) / 64;   // load instructions per K (or V) tile
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  __bf16 E2D2_LDS* lds = (__bf16 E2D2_LDS*)smem_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -80,19 +76,29 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
   const int t_end = (int)((long long)p.n_tiles * (split + 1) / p.n_split);
 
   const size_t kv_bh = (size_t)b * p.Hkv + hk;
-  const __bf16* kc = p.k_cache + kv_bh * (size_t)p.cap * D;
-  const __bf16* vc = p.v_cache + kv_bh * (size_t)p.cap * D;
-  const __bf16* kbk = p.k_blk + kv_bh * (size_t)S * D;
-  const __bf16* vbk = p.v_blk + kv_bh * (size_t)S * D;
+  const __amdgpu_buffer_rsrc_t rkc = make_rsrc(p.k_cache + kv_bh * (size_t)p.cap * D, (uint32_t)C * D * 2u);
+  const __amdgpu_buffer_rsrc_t rvc = make_rsrc(p.v_cache + kv_bh * (size_t)p.cap * D, (uint32_t)C * D * 2u);
+  const __amdgpu_buffer_rsrc_t rkb = make_rsrc(p.k_blk + kv_bh * (size_t)S * D, (uint32_t)S * D * 2u);
+  const __amdgpu_buffer_rsrc_t rvb = make_rsrc(p.v_blk + kv_bh * (size_t)S * D, (uint32_t)S * D * 2u);
+  TileLoader<D, kTN, 1> loader;  // each wave loads its own tiles
+  loader.init(0, lane);
 
-  __bf16 E2D2_LDS* my = lds + wave * (2 * 2 * TILE);  // [stage][K, V][TILE]
+  char E2D2_LDS* my = (char E2D2_LDS*)smem_raw + wave * (2 * 2 * TILE * 2);  // [stage][K, V]
   auto issue = [&](int t, int stage) {
-    __bf16 E2D2_LDS* kt = my + stage * 2 * TILE;
-    const bool cache = t < p.n_tiles_cache;
-    const int c = cache ? t : t - p.n_tiles_cache;
-    load_tile_lds<D, kTN>(cache ? kc : kbk, c * kTN, cache ? C : S, kt, 0, 1, lane);
-    load_tile_lds<D, kTN>(cache ? vc : vbk, c * kTN, cache ? C : S, kt + TILE, 0, 1, lane);
+    char E2D2_LDS* kt = my + stage * 2 * TILE * 2;
+    if (t < p.n_tiles_cache) {
+      loader.load(rkc, t * kTN, kt, 0);
+      loader.load(rvc, t * kTN, kt + TILE * 2, 0);
+    } else {
+      loader.load(rkb, (t - p.n_tiles_cache) * kTN, kt, 0);
+      loader.load(rvb, (t - p.n_tiles_cache) * kTN, kt + TILE * 2, 0);
+    }
   };
+  uint32_t offA[NDB], offB[NDB];
+  vt_offsets<D>(lane, offA, offB);
+  uint32_t koff[NC];
+  k_offsets<D>(lane, koff);
+  const uint32_t my0 = lds_addr(my);
 
   // ---- queries
   bf16x8 qf[kNQB][NC];
@@ -114,10 +120,10 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
   }
 
   f32x16 o[kNQB][NDB];
-  float m[kNQB], l[kNQB];
+  float m[kNQB], l[kNQB];  // m: running max in use, base-2 units; l: lane-partial sum
 #pragma unroll
   for (int i = 0; i < kNQB; ++i) {
-    m[i] = -INFINITY;
+    m[i] = -1e30f;
     l[i] = 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[i][db] = zero16();
@@ -133,12 +139,11 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
     const int t = first + i * kWaves;
     if (i + 1 < n_my) {
       issue(t + kWaves, (i + 1) & 1);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+      wait_vmem<2 * NI>();
     } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wait_vmem<0>();
     }
-    const __bf16 E2D2_LDS* kt = my + (i & 1) * 2 * TILE;
-    const __bf16 E2D2_LDS* vt = kt + TILE;
+    const char E2D2_LDS* kt = my + (i & 1) * 2 * TILE * 2;
     const bool cache = t < p.n_tiles_cache;
     const int k0 = (cache ? t : t - p.n_tiles_cache) * kTN;
     const int n = cache ? C : S;
@@ -146,7 +151,9 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
 
     bf16x8 kf[NC];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) kf[cc] = read_k_frag<D>(kt, 0, cc * 16, lane);
+    for (int cc = 0; cc < NC; ++cc) kf[cc] = *(const bf16x8 E2D2_LDS*)(kt + koff[cc]);
+    bf16x8 vf[2][NDB];
+    read_vt_tile32<D>(my0 + (uint32_t)((i & 1) * 2 * TILE * 2 + TILE * 2), offA, offB, vf);
 
 #pragma unroll
     for (int qi = 0; qi < kNQB; ++qi) {
@@ -163,30 +170,35 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[qi], mx);
-      const float base = m_new * c;  // finite: every tile holds >= 1 key
-      const float alpha = fast_exp2(m[qi] * c - base);
+      // lazy, per-row rescale: keep the running max unless the row max grew by > 2^8
+      const float rmax = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = rmax * c > m[qi] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        if (need) {
+          const float m_new = rmax * c;
+          const float alpha = fast_exp2(m[qi] - m_new);
+          l[qi] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[qi][db][j] *= alpha;
+          m[qi] = m_new;
+        }
+      }
       float rs = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(fmaf(sc[j], c, -base));
+        const float e = fast_exp2(fmaf(sc[j], c, -m[qi]));
         sc[j] = e;
         rs += e;
       }
-      l[qi] = l[qi] * alpha + rs;
-      m[qi] = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[qi][db][j] *= alpha;
+      l[qi] += rs;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const bf16x8 pb = to_bf16x8(sc[h * 8], sc[h * 8 + 1], sc[h * 8 + 2], sc[h * 8 + 3],
                                     sc[h * 8 + 4], sc[h * 8 + 5], sc[h * 8 + 6], sc[h * 8 + 7]);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          o[qi][db] = mfma32(read_vt_frag<D>(vt, h * 16, db * 32, lane), pb, o[qi][db]);
+        for (int db = 0; db < NDB; ++db) o[qi][db] = mfma32(vf[h][db], pb, o[qi][db]);
       }
     }
   }
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
   const int row = lane & 31;
 #pragma unroll
   for (int qi = 0; qi < kNQB; ++qi) {
-    const float ms = n_my > 0 ? m[qi] * c : -INFINITY;
+    const float ms = n_my > 0 ? m[qi] : -INFINITY;
     if (lane < 32) mw[(wave * kNQB + qi) * 32 + row] = ms;
     lw[(wave * kNQB + qi) * 64 + lane] = n_my > 0 ? l[qi] : 0.f;
   }

@@ -12,18 +12,23 @@
 //   * Each wave owns 32 query rows and keeps their Q fragments in registers.
 //   * The key axis is walked one 64-key tile at a time, source by source (clean
 //     context keys, then, for the decoder, the noised keys of the own blocks), over
-//     exactly the tiles that hold an allowed pair (schedule.h).  K and V tiles are
-//     loaded straight from HBM into a double-buffered, swizzled LDS tile with
-//     global_load_lds_dwordx4 while the previous tile is being computed.
+//     exactly the tiles that hold an allowed pair (schedule.h).  K and V tiles go from
+//     HBM straight into a 4-deep ring of swizzled LDS stages (buffer_load ... lds);
+//     tile t+3 is in flight while tile t is computed.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so a
 //     lane holds 16 keys of ONE query row: the row max is an in-lane reduction plus one
 //     exchange with lane l^32, and the row sum needs no exchange until the end.
-//   * Online softmax in base 2 with the scale folded in (p = 2^(s*c - m*c), c =
-//     scale*log2 e), p rounded to bf16, then O^T += V^T P^T on the MFMA with V^T read
-//     by the transposing LDS read; fp32 accumulation throughout.
+//   * The loop is software-pipelined: the MFMAs of S^T for tile t+1 are issued next to
+//     the softmax of tile t, then O^T += V^T P^T for tile t (V^T from the transposing
+//     LDS read).
+//   * Online softmax in base 2 with the scale folded in (p = 2^(s*c - m), c =
+//     scale*log2 e) and lazy rescaling: a row keeps its running max m until its scores
+//     exceed it by more than 2^8, so O and l are rescaled only on those rare tiles (the
+//     result is the same softmax; p <= 2^8 stays well inside bf16 and fp32 range).
+//     The decision is per row, so a row's arithmetic depends on its own keys only.
 //   * Within a tile, each wave classifies its 32x32 key blocks: empty blocks are
 //     skipped (no MFMA), full blocks skip the mask, the rest mask per element.
-//   * Epilogue: O = O^T / l in bf16, LSE = scale * m + ln l in fp32.
+//   * Epilogue: O = O^T / l in bf16, LSE = (m + log2 l) ln 2 in fp32.
 //   * Work order: query tiles are issued from the last (most keys) to the first;
 //     when the number of (head, kind) items per tile level is a multiple of 8, each of
 //     the 8 XCDs gets a fixed contiguous set of heads so that a head's K/V tiles stay
@@ -38,19 +43,30 @@ namespace {
 constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kWaves = 4;
+constexpr int kStages = 4;        // LDS ring depth: tile t+3 is loaded while t is computed
+constexpr float kLazy = 8.f;      // rescale only when a row max grows by > 2^8
+constexpr float kNegBig = -1e30f; // "no key yet" running max (finite: no inf - inf)
 
 template <int D>
-__global__ __launch_bounds__(256) void train_fwd_bf16_kernel(TrainParams p) {
-  constexpr int NC = D / 16;   // MFMA k-steps over the head dim for S^T
-  constexpr int NDB = D / 32;  // 32-wide head-dim blocks of O^T
-  constexpr int TILE = kBN * D;
+struct Geo {
+  static constexpr int NC = D / 16;   // MFMA k-steps over the head dim for S^T
+  static constexpr int NDB = D / 32;  // 32-wide head-dim blocks of O^T
+  static constexpr int TILE = kBN * D;  // bf16 elements of one K or V tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int NIW = 2 * (kBN * (D / 8) / 64) / kWaves;  // loads per wave per tile
+};
+
+template <int D>
+__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void train_fwd_bf16_kernel(TrainParams p) {
+  using G = Geo<D>;
+  constexpr int NC = G::NC, NDB = G::NDB, TILE = G::TILE, STAGE = G::STAGE, NIW = G::NIW;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  __bf16 E2D2_LDS* lds = (__bf16 E2D2_LDS*)smem_raw;  // [2 buffers][K, V][TILE]
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
 
-  // ---- work item
+  // ---- work item: query tiles from the last (most keys) to the first; heads grouped
+  //      per XCD when the item count of a tile level is a multiple of 8
   const int BH = p.B * p.Hq;
   const int per_level = BH * p.n_kinds;
   const int w = blockIdx.x;
@@ -82,19 +98,29 @@ __global__ __launch_bounds__(256) void train_fwd_bf16_kernel(TrainParams p) {
   const int ntot = n0 + (tr1.last - tr1.first);
 
   const size_t kv_off = ((size_t)b * p.Hkv + hk) * (size_t)L * D;
-  const __bf16* kbase[2] = {p.k[0] + kv_off, p.k[1] + kv_off};
-  const __bf16* vbase[2] = {p.v[0] + kv_off, p.v[1] + kv_off};
+  const uint32_t kv_bytes = (uint32_t)L * D * 2u;
+  const __amdgpu_buffer_rsrc_t rk0 = make_rsrc(p.k[0] + kv_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv0 = make_rsrc(p.v[0] + kv_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rk1 = make_rsrc(p.k[1] + kv_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv1 = make_rsrc(p.v[1] + kv_off, kv_bytes);
+  TileLoader<D, kBN, kWaves> loader;
+  loader.init(wave, lane);
+  char E2D2_LDS* lds_b = (char E2D2_LDS*)smem_raw;
 
-  auto issue = [&](int t, int buf) {
-    const int src = t < n0 ? 0 : 1;
-    const int c = src == 0 ? tr0.first + t : tr1.first + (t - n0);
-    __bf16 E2D2_LDS* kt = lds + (2 * buf) * TILE;
-    __bf16 E2D2_LDS* vt = kt + TILE;
-    load_tile_lds<D, kBN>(kbase[src], c * kBN, L, kt, wave, kWaves, lane);
-    load_tile_lds<D, kBN>(vbase[src], c * kBN, L, vt, wave, kWaves, lane);
+  // tile index -> (source, key-tile number in that source)
+  auto tsrc = [&](int t) { return t < n0 ? 0 : 1; };
+  auto tnum = [&](int t) { return t < n0 ? tr0.first + t : tr1.first + (t - n0); };
+  auto issue = [&](int t) {
+    char E2D2_LDS* kt = lds_b + (t % kStages) * STAGE * 2;
+    const int row0 = tnum(t) * kBN;
+    if (t < n0) {
+      loader.load(rk0, row0, kt, wave);
+      loader.load(rv0, row0, kt + TILE * 2, wave);
+    } else {
+      loader.load(rk1, row0, kt, wave);
+      loader.load(rv1, row0, kt + TILE * 2, wave);
+    }
   };
-
-  if (ntot > 0) issue(0, 0);
 
   // ---- per-wave rows and per-lane query row
   const int wq0 = q0 + wave * 32;
@@ -104,10 +130,40 @@ __global__ __launch_bounds__(256) void train_fwd_bf16_kernel(TrainParams p) {
   const bool row_ok = qi < L;
   Interval iv[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    iv[s] = row_interval(kind, s, row_ok ? qi : 0, S, L, 0);
-    if (!row_ok) iv[s] = Interval{0, 0};
+  for (int sidx = 0; sidx < 2; ++sidx) {
+    iv[sidx] = row_interval(kind, sidx, row_ok ? qi : 0, S, L, 0);
+    if (!row_ok) iv[sidx] = Interval{0, 0};
   }
+  // Classification of the two 32-key blocks of tile t for this wave:
+  // 0 = no allowed pair (skipped), 1 = partly allowed (masked), 2 = all allowed.
+  // The keys the wave's rows allow at all (union) and allow in every row (common) are
+  // fixed per source, so a block is classified with four compares.
+  Interval wu[2] = {{0, 0}, {0, 0}}, wc[2] = {{0, 0}, {0, 0}};
+  if (wave_live) {
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      if (sidx < nsrc) {
+        wu[sidx] = union_interval(kind, sidx, wq0, wr1, S, L, 0);
+        wc[sidx] = common_interval(kind, sidx, wq0, wr1, S, L, 0);
+      }
+    }
+  }
+  auto classify_tile = [&](int t, int (&cls)[2]) {
+    const int src = tsrc(t);
+    const Interval u = src ? wu[1] : wu[0];
+    const Interval cm = src ? wc[1] : wc[0];
+    const int kt0 = tnum(t) * kBN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int k0 = kt0 + kb * 32;
+      const int k1 = min(k0 + 32, L);
+      int cl;
+      if (k1 <= u.lo || k0 >= u.hi || k1 <= k0) cl = 0;
+      else if (cm.lo <= k0 && k1 <= cm.hi && k1 - k0 == 32) cl = 2;
+      else cl = 1;
+      cls[kb] = cl;
+    }
+  };
 
   const size_t q_off = ((size_t)b * p.Hq + hq) * (size_t)L * D;
   bf16x8 qf[NC];
@@ -123,53 +179,50 @@ __global__ __launch_bounds__(256) void train_fwd_bf16_kernel(TrainParams p) {
       qf[cc] = v;
     }
   }
+  uint32_t offA[NDB], offB[NDB];
+  vt_offsets<D>(lane, offA, offB);
+  uint32_t koff[NC];
+  k_offsets<D>(lane, koff);
+  const uint32_t lds0 = lds_addr(lds_b);
 
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = zero16();
-  float m = -INFINITY;  // running max of raw scores q.k
-  float l = 0.f;        // lane-partial running sum
+  float ms = kNegBig;  // running max in use, in base-2 units (raw max * c)
+  float l = 0.f;       // lane-partial running sum, relative to ms
   const float c = p.c;
 
-  for (int t = 0; t < ntot; ++t) {
-    const int buf = t & 1;
-    wait_vmem_all();
-    __syncthreads();  // tile t is in LDS for every wave; buffer buf^1 is free
-    if (t + 1 < ntot) issue(t + 1, buf ^ 1);
-
-    const int src = t < n0 ? 0 : 1;
-    const int ct = src == 0 ? tr0.first + t : tr1.first + (t - n0);
-    const __bf16 E2D2_LDS* kt = lds + (2 * buf) * TILE;
-    const __bf16 E2D2_LDS* vt = kt + TILE;
-    if (!wave_live) continue;
-
-    f32x16 sc[2];
-    int cls[2];
+  // S^T of tile t for this wave (blocks with cls == 0 are left untouched).
+  auto qk = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
+    const char E2D2_LDS* kt = lds_b + (t % kStages) * STAGE * 2;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int k0 = ct * kBN + kb * 32;
-      const int k1 = min(k0 + 32, L);
-      int cl = classify(kind, src, wq0, wr1, S, L, 0, k0, k1);
-      if (cl == 2 && k1 - k0 < 32) cl = 1;
-      cls[kb] = cl;
-      if (cl) {
+      if (cls[kb]) {
         f32x16 acc = zero16();
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc)
-          acc = mfma32(read_k_frag<D>(kt, kb * 32, cc * 16, lane), qf[cc], acc);
-        if (cl == 1) {
-          const int kr = k0 + ((lane >> 5) << 2);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = kr + ((j >> 2) << 3) + (j & 3);
-            if (key < iv[src].lo || key >= iv[src].hi) acc[j] = -INFINITY;
-          }
-        }
+          acc = mfma32(*(const bf16x8 E2D2_LDS*)(kt + kb * 64 * D + koff[cc]), qf[cc], acc);
         sc[kb] = acc;
       }
     }
-    if (!cls[0] && !cls[1]) continue;
-
+  };
+  // Mask, online softmax (lazy rescale), P in bf16, then O^T += V^T P^T for tile t.
+  auto softmax_pv = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
+    const int src = tsrc(t);
+    const int kt0 = tnum(t) * kBN;
+    bf16x8 vf[4][NDB];
+    read_vt_tile64<D>(lds0 + 2u * (uint32_t)((t % kStages) * STAGE + TILE), offA, offB, vf);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (cls[kb] == 1) {
+        const int kr = kt0 + kb * 32 + ((lane >> 5) << 2);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kr + ((j >> 2) << 3) + (j & 3);
+          if (key < iv[src].lo || key >= iv[src].hi) sc[kb][j] = -INFINITY;
+        }
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -177,43 +230,81 @@ __global__ __launch_bounds__(256) void train_fwd_bf16_kernel(TrainParams p) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float base = m_new == -INFINITY ? 0.f : m_new * c;
-    const float alpha = fast_exp2(m * c - base);
-    float rs = 0.f;
+    // Per-row decision (both lanes of a row see the row max), so a row's arithmetic
+    // depends only on its own allowed keys.
+    const float rmax = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = rmax * c > ms + kLazy;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      if (need) {
+        const float m_new = rmax * c;
+        const float alpha = fast_exp2(ms - m_new);
+        l *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (cls[kb]) {
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = fast_exp2(fmaf(sc[kb][j], c, -base));
-          sc[kb][j] = e;
-          rs += e;
-        }
+          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        ms = m_new;
       }
-    l = l * alpha + rs;
-    m = m_new;
+    }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kb = 0; kb < 2; ++kb) {
+      if (!cls[kb]) continue;
+      float rs = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+      for (int j = 0; j < 16; ++j) {
+        const float e = fast_exp2(fmaf(sc[kb][j], c, -ms));
+        sc[kb][j] = e;
+        rs += e;
+      }
+      l += rs;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j0 = h * 8;
+        const bf16x8 pb = to_bf16x8(sc[kb][j0], sc[kb][j0 + 1], sc[kb][j0 + 2], sc[kb][j0 + 3],
+                                    sc[kb][j0 + 4], sc[kb][j0 + 5], sc[kb][j0 + 6], sc[kb][j0 + 7]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = mfma32(vf[kb * 2 + h][db], pb, o[db]);
+      }
+    }
+  };
 
+  // ---- prologue: tiles 0 .. kStages-2 in flight, tile 0 landed, S^T of tile 0
+  f32x16 sA[2], sB[2];
+  int cA[2] = {0, 0}, cB[2] = {0, 0};
+  if (ntot > 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (cls[kb]) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int j0 = h * 8;
-          const bf16x8 pb = to_bf16x8(sc[kb][j0], sc[kb][j0 + 1], sc[kb][j0 + 2], sc[kb][j0 + 3],
-                                      sc[kb][j0 + 4], sc[kb][j0 + 5], sc[kb][j0 + 6],
-                                      sc[kb][j0 + 7]);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            o[db] = mfma32(read_vt_frag<D>(vt, kb * 32 + h * 16, db * 32, lane), pb, o[db]);
-        }
-      }
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < ntot) issue(i);
+    const int after0 = min(kStages - 2, ntot - 1);  // tiles issued after tile 0
+    if (after0 >= 2) wait_vmem<2 * NIW>();
+    else if (after0 == 1) wait_vmem<NIW>();
+    else wait_vmem<0>();
+    __syncthreads();
+    classify_tile(0, cA);
+    qk(0, cA, sA);
   }
+
+  // ---- main loop, unrolled by two so the score buffers alternate without copies
+  auto step = [&](int t, int (&cc)[2], f32x16 (&scur)[2], int (&cn)[2], f32x16 (&snext)[2]) {
+    if (t + 1 < ntot) {
+      // tile t+1 must have landed; tiles issued after it may stay in flight
+      if (t + 2 < ntot) wait_vmem<NIW>();
+      else wait_vmem<0>();
+    }
+    __syncthreads();  // everyone is done with tile t-1; its stage is free
+    if (t + kStages - 1 < ntot) issue(t + kStages - 1);
+    if (t + 1 < ntot) {
+      classify_tile(t + 1, cn);
+      qk(t + 1, cn, snext);
+    }
+    softmax_pv(t, cc, scur);
+  };
+  int t = 0;
+  for (; t + 1 < ntot; t += 2) {
+    step(t, cA, sA, cB, sB);
+    step(t + 1, cB, sB, cA, sA);
+  }
+  if (t < ntot) step(t, cA, sA, cB, sB);
 
   // ---- epilogue
   const float l_tot = l + __shfl_xor(l, 32);
@@ -233,7 +324,8 @@ __global__ __launch_bounds__(256) void train_fwd_bf16_kernel(TrainParams p) {
         *(bf16x4*)(orow + d) = v;
       }
     if (p.lse[slot] != nullptr && lane < 32)
-      p.lse[slot][((size_t)b * p.Hq + hq) * L + qi] = m * p.scale + logf(l_tot);
+      p.lse[slot][((size_t)b * p.Hq + hq) * L + qi] =
+          (ms + __log2f(l_tot)) * 0.6931471805599453f;
   }
   if (p.visits != nullptr && threadIdx.x == 0) atomicAdd(p.visits, (unsigned long long)ntot);
 }
@@ -335,7 +427,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
 
 template <int D>
 hipError_t launch_train_bf16_d(const TrainParams& p, int grid, hipStream_t stream) {
-  const size_t smem = (size_t)2 * 2 * kBN * D * sizeof(__bf16);
+  const size_t smem = (size_t)kStages * Geo<D>::STAGE * sizeof(__bf16);
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)train_fwd_bf16_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

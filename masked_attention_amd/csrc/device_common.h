@@ -99,6 +99,54 @@ __device__ __forceinline__ void load_tile_lds(const __bf16* __restrict__ src, in
   }
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled, 32-bit records).  Loads
+// past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Direct buffer->LDS loads of a ROWS x D bf16 tile into the swizzled layout, split
+// over NWAVES waves.  Per lane, the byte offsets inside a tile do not depend on the
+// tile, so they are computed once (init); per tile only the scalar row offset
+// changes.  Rows past the buffer's end read as zero.
+template <int D, int ROWS, int NWAVES>
+struct TileLoader {
+  static constexpr int CH = D / 8;
+  static constexpr int NI = ROWS * CH / 64;  // 1 KiB instructions per tile
+  static constexpr int NPW = NI / NWAVES;    // per wave
+  static_assert(NI % NWAVES == 0 && ROWS * CH % 64 == 0, "tile does not split evenly");
+  uint32_t voff[NPW];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < NPW; ++k) {
+      const int slot = (wave + k * NWAVES) * 64 + lane;
+      const int r = slot / CH;
+      const int lc = (slot % CH) ^ swz<D>(r);
+      voff[k] = (uint32_t)(r * D + lc * 8) * 2u;
+    }
+  }
+  // tile: LDS destination (uniform); row0: first row of the tile in the buffer.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int row0, char E2D2_LDS* tile,
+                                       int wave) const {
+#pragma unroll
+    for (int k = 0; k < NPW; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void E2D2_LDS*)(tile + (wave + k * NWAVES) * 1024),
+                                               16, (int)voff[k], row0 * D * 2, 0, 0);
+  }
+};
+
+// Per-lane byte offsets of the K operand reads (S^T = K Q^T): koff[cc] addresses
+// K[l % 32][16 cc + 8 (l / 32) ..+7] in a swizzled tile; the 32-key block kb sits
+// 64 * D * kb bytes further (rows 32 apart share the swizzle).
+template <int D>
+__device__ __forceinline__ void k_offsets(int lane, uint32_t (&koff)[D / 16]) {
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc)
+    koff[cc] = 2u * (uint32_t)tile_off<D>(lane & 31, cc * 16 + ((lane >> 5) << 3));
+}
+
 // MFMA A-operand read of K for S^T = K Q^T: lane l gets K[row0 + l%32][col0 + 8*(l/32) ..+7].
 template <int D>
 __device__ __forceinline__ bf16x8 read_k_frag(const __bf16 E2D2_LDS* tile, int row0, int col0,
@@ -133,5 +181,175 @@ __device__ __forceinline__ bf16x8 read_vt_frag(const __bf16 E2D2_LDS* tile, int 
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------------
+// Transposing LDS reads of V in one asm block that also waits for them.  Written as
+// inline asm (not the builtin) because the compiler cannot tell these reads apart from
+// the in-flight global_load_lds writes of later tiles and would otherwise wait for ALL
+// outstanding vector-memory loads before each of them, which serialises the prefetch.
+// The tiles read here are complete: the caller waited for their loads (wait_vmem) and
+// passed a workgroup barrier where other waves loaded them.  Each asm block ends with
+// s_waitcnt lgkmcnt(0), so its outputs are valid when it completes.
+//
+// tr_reads<N, OFF>: for each of the N byte addresses a[i] (LDS), reads 8 bytes at a[i]
+// and at a[i] + OFF; o[2i] gets the first, o[2i+1] the second.
+template <int OFF>
+__device__ __forceinline__ void tr_reads(const uint32_t (&a)[2], long (&o)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a[0]), "v"(a[1]), "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void tr_reads(const uint32_t (&a)[4], long (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void tr_reads(const uint32_t (&a)[8], long (&o)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]),
+        "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+        "v"(a[7]), "i"(OFF)
+      : "memory");
+}
+
+__device__ __forceinline__ bf16x8 join_bf16(long lo, long hi) {
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
+                                 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per-lane byte offsets, inside a swizzled V tile, of the two transposing reads that
+// give lane l its V^T operand for keys [0, 16) and head dims [32*db, 32*db + 32); the
+// operands of keys [16j, 16j + 16) sit 32*D*j bytes further (rows 16 apart share the
+// swizzle).  See read_vt_frag for the key order.
+template <int D>
+__device__ __forceinline__ void vt_offsets(int lane, uint32_t (&offA)[D / 32],
+                                           uint32_t (&offB)[D / 32]) {
+  const int g = lane >> 5;
+  const int s = lane & 15;
+  const int r_a = (g << 2) + (s >> 2);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = db * 32 + (((lane >> 4) & 1) << 4) + ((s & 3) << 2);
+    offA[db] = 2u * (uint32_t)tile_off<D>(r_a, col);
+    offB[db] = 2u * (uint32_t)tile_off<D>(r_a + 8, col);
+  }
+}
+
+// V^T operands of a whole 64-key tile at LDS byte address vbase: vf[j][db] covers keys
+// [16j, 16j + 16) and head dims [32 db, 32 db + 32).
+template <int D>
+__device__ __forceinline__ void read_vt_tile64(uint32_t vbase, const uint32_t (&offA)[D / 32],
+                                               const uint32_t (&offB)[D / 32],
+                                               bf16x8 (&vf)[4][D / 32]) {
+  constexpr int NDB = D / 32;
+  constexpr int OFF = 32 * D;  // 16 rows
+  if constexpr (NDB == 1) {
+    const uint32_t a[4] = {vbase + offA[0], vbase + offA[0] + 2 * OFF, vbase + offB[0],
+                           vbase + offB[0] + 2 * OFF};
+    long o[8];
+    tr_reads<OFF>(a, o);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vf[j][0] = join_bf16(o[j], o[4 + j]);
+  } else {
+#pragma unroll
+    for (int dp = 0; dp < NDB; dp += 2) {
+      const uint32_t a[8] = {vbase + offA[dp], vbase + offA[dp] + 2 * OFF, vbase + offB[dp],
+                             vbase + offB[dp] + 2 * OFF, vbase + offA[dp + 1],
+                             vbase + offA[dp + 1] + 2 * OFF, vbase + offB[dp + 1],
+                             vbase + offB[dp + 1] + 2 * OFF};
+      long o[16];
+      tr_reads<OFF>(a, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vf[j][dp] = join_bf16(o[j], o[4 + j]);
+        vf[j][dp + 1] = join_bf16(o[8 + j], o[12 + j]);
+      }
+    }
+  }
+}
+
+// V^T operands of a 32-key tile: vf[j][db] covers keys [16j, 16j + 16), j = 0, 1.
+template <int D>
+__device__ __forceinline__ void read_vt_tile32(uint32_t vbase, const uint32_t (&offA)[D / 32],
+                                               const uint32_t (&offB)[D / 32],
+                                               bf16x8 (&vf)[2][D / 32]) {
+  constexpr int NDB = D / 32;
+  constexpr int OFF = 32 * D;
+  if constexpr (NDB == 1) {
+    const uint32_t a[2] = {vbase + offA[0], vbase + offB[0]};
+    long o[4];
+    tr_reads<OFF>(a, o);
+    vf[0][0] = join_bf16(o[0], o[2]);
+    vf[1][0] = join_bf16(o[1], o[3]);
+  } else if constexpr (NDB == 2) {
+    const uint32_t a[4] = {vbase + offA[0], vbase + offB[0], vbase + offA[1], vbase + offB[1]};
+    long o[8];
+    tr_reads<OFF>(a, o);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      vf[0][db] = join_bf16(o[4 * db], o[4 * db + 2]);
+      vf[1][db] = join_bf16(o[4 * db + 1], o[4 * db + 3]);
+    }
+  } else {
+    const uint32_t a[8] = {vbase + offA[0], vbase + offB[0], vbase + offA[1], vbase + offB[1],
+                           vbase + offA[2], vbase + offB[2], vbase + offA[3], vbase + offB[3]};
+    long o[16];
+    tr_reads<OFF>(a, o);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      vf[0][db] = join_bf16(o[4 * db], o[4 * db + 2]);
+      vf[1][db] = join_bf16(o[4 * db + 1], o[4 * db + 3]);
+    }
+  }
+}
+
+// LDS byte address of an LDS pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void E2D2_LDS* p) {
+  return (uint32_t)(uintptr_t)p;
+}
 
 }  // namespace e2d2
