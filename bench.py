@@ -13,7 +13,7 @@ Also measured in the same run and reported in the same JSON line:
   * ``denoise``: the inference step at B=32, 16 query / 8 KV heads, d_head 128, cache
     2048, block S=32: 32 denoising steps with fresh block tensors, then the KV-cache
     append; microseconds per step and algorithmic GB/s, with the Infinity Cache warm
-    (steady state) and flushed before every step (cold);
+    (steady state) and swept out by a 1 GiB read before every step (cold);
   * ``long_train``: the same training forward at B=2, 16/8 heads, d_head 128, L=8192,
     S=64, with LSE (MFMA-bound);
   * ``roofline``: the training kernel's useful TFLOP/s against the bf16 MFMA peak,
@@ -162,11 +162,14 @@ def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
             step_ms.append(ms)
         _, ms = timed_launches(append, 1, stream)
         append_ms.append(ms)
-    # cold: flush the 256 MB Infinity Cache (and L2) with a 1 GiB write before each step
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # cold: before each step, sweep a 1 GiB buffer with reads only, so the 256 MB
+    # Infinity Cache and the L2 hold other, clean lines (a write sweep would leave dirty
+    # lines whose write-back would be charged to the step)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
     cold_ms = []
     for t in range(min(T, 16)):
-        flush.zero_()
+        flush.sum()
         _, ms = timed_launches(lambda: step(t), 1, stream)
         cold_ms.append(ms)
     del flush

@@ -143,35 +143,41 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
     } else {
       wait_vmem<0>();
     }
-    const char E2D2_LDS* kt = my + (i & 1) * 2 * TILE * 2;
     const bool cache = t < p.n_tiles_cache;
     const int k0 = (cache ? t : t - p.n_tiles_cache) * kTN;
     const int n = cache ? C : S;
     const bool ragged = k0 + kTN > n;
 
+    // K operands once per tile, then S^T of every column block back to back.
+    const uint32_t kb_addr = my0 + (uint32_t)((i & 1) * 2 * TILE * 2);
     bf16x8 kf[NC];
+    kread_block<D, 0>(kb_addr, koff, kf);
+    f32x16 sc[kNQB];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) kf[cc] = *(const bf16x8 E2D2_LDS*)(kt + koff[cc]);
+    for (int qi = 0; qi < kNQB; ++qi) {
+      if (qi >= nq) break;
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) acc = mfma32(kf[cc], qf[qi][cc], acc);
+      sc[qi] = acc;
+    }
     bf16x8 vf[2][NDB];
-    read_vt_tile32<D>(my0 + (uint32_t)((i & 1) * 2 * TILE * 2 + TILE * 2), offA, offB, vf);
+    read_vt_tile32<D>(kb_addr + (uint32_t)(TILE * 2), offA, offB, vf);
 
 #pragma unroll
     for (int qi = 0; qi < kNQB; ++qi) {
       if (qi >= nq) break;
-      f32x16 sc = zero16();
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) sc = mfma32(kf[cc], qf[qi][cc], sc);
       if (ragged) {
         const int kr = k0 + ((lane >> 5) << 2);
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (kr + ((j >> 2) << 3) + (j & 3) >= n) sc[j] = -INFINITY;
+          if (kr + ((j >> 2) << 3) + (j & 3) >= n) sc[qi][j] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[j]);
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[qi][j]);
       // lazy, per-row rescale: keep the running max unless the row max grew by > 2^8
-      const float rmax = fmaxf(mx, __shfl_xor(mx, 32));
+      const float rmax = pair_max(mx);
       const bool need = rmax * c > m[qi] + 8.f;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         if (need) {
@@ -188,15 +194,16 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
       float rs = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(fmaf(sc[j], c, -m[qi]));
-        sc[j] = e;
+        const float e = fast_exp2(fmaf(sc[qi][j], c, -m[qi]));
+        sc[qi][j] = e;
         rs += e;
       }
       l[qi] += rs;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8 pb = to_bf16x8(sc[h * 8], sc[h * 8 + 1], sc[h * 8 + 2], sc[h * 8 + 3],
-                                    sc[h * 8 + 4], sc[h * 8 + 5], sc[h * 8 + 6], sc[h * 8 + 7]);
+        const bf16x8 pb = to_bf16x8(sc[qi][h * 8], sc[qi][h * 8 + 1], sc[qi][h * 8 + 2],
+                                    sc[qi][h * 8 + 3], sc[qi][h * 8 + 4], sc[qi][h * 8 + 5],
+                                    sc[qi][h * 8 + 6], sc[qi][h * 8 + 7]);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[qi][db] = mfma32(vf[h][db], pb, o[qi][db]);
       }

@@ -43,7 +43,16 @@ namespace {
 constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kWaves = 4;
-constexpr int kStages = 4;        // LDS ring depth: tile t+3 is loaded while t is computed
+// Loop structure per head dimension (measured on MI355X): at d <= 64 the registers of a
+// simple tile-at-a-time loop allow 3 waves per SIMD (3-deep LDS ring), whose interleaving
+// overlaps one wave's softmax with another's MFMAs; at d = 128 the accumulators allow a
+// single wave per SIMD, so the loop is software-pipelined instead (4-deep ring).
+template <int D>
+struct LoopCfg {
+  static constexpr bool kPipelined = D > 64;
+  static constexpr int kStages = D > 64 ? 4 : 3;
+  static constexpr int kOccupancy = D > 64 ? 1 : 3;
+};
 constexpr float kLazy = 8.f;      // rescale only when a row max grows by > 2^8
 constexpr float kNegBig = -1e30f; // "no key yet" running max (finite: no inf - inf)
 
@@ -57,8 +66,9 @@ struct Geo {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void train_fwd_bf16_kernel(TrainParams p) {
+__global__ __launch_bounds__(256, LoopCfg<D>::kOccupancy) void train_fwd_bf16_kernel(TrainParams p) {
   using G = Geo<D>;
+  constexpr int kStages = LoopCfg<D>::kStages;
   constexpr int NC = G::NC, NDB = G::NDB, TILE = G::TILE, STAGE = G::STAGE, NIW = G::NIW;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
 
@@ -194,24 +204,14 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void train_fwd_bf16_kernel(
 
   // S^T of tile t for this wave (blocks with cls == 0 are left untouched).
   auto qk = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
-    const char E2D2_LDS* kt = lds_b + (t % kStages) * STAGE * 2;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (cls[kb]) {
-        f32x16 acc = zero16();
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
-          acc = mfma32(*(const bf16x8 E2D2_LDS*)(kt + kb * 64 * D + koff[cc]), qf[cc], acc);
-        sc[kb] = acc;
-      }
-    }
+    const int want = (cls[0] ? 1 : 0) | (cls[1] ? 2 : 0);
+    if (want) qk_blocks<D, 2>(lds0 + 2u * (uint32_t)((t % kStages) * STAGE), koff, qf, sc, want);
   };
   // Mask, online softmax (lazy rescale), P in bf16, then O^T += V^T P^T for tile t.
   auto softmax_pv = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
     const int src = tsrc(t);
     const int kt0 = tnum(t) * kBN;
-    bf16x8 vf[4][NDB];
-    read_vt_tile64<D>(lds0 + 2u * (uint32_t)((t % kStages) * STAGE + TILE), offA, offB, vf);
+    const uint32_t vb = lds0 + 2u * (uint32_t)((t % kStages) * STAGE + TILE);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (cls[kb] == 1) {
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void train_fwd_bf16_kernel(
       }
     // Per-row decision (both lanes of a row see the row max), so a row's arithmetic
     // depends only on its own allowed keys.
-    const float rmax = fmaxf(mx, __shfl_xor(mx, 32));
+    const float rmax = pair_max(mx);
     const bool need = rmax * c > ms + kLazy;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       if (need) {
@@ -257,57 +257,169 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void train_fwd_bf16_kernel(
         rs += e;
       }
       l += rs;
+      bf16x8 vf[2][NDB];
+      read_vt_tile32<D>(vb + (uint32_t)(kb * 64 * D), offA, offB, vf);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j0 = h * 8;
         const bf16x8 pb = to_bf16x8(sc[kb][j0], sc[kb][j0 + 1], sc[kb][j0 + 2], sc[kb][j0 + 3],
                                     sc[kb][j0 + 4], sc[kb][j0 + 5], sc[kb][j0 + 6], sc[kb][j0 + 7]);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] = mfma32(vf[kb * 2 + h][db], pb, o[db]);
+        for (int db = 0; db < NDB; ++db) o[db] = mfma32(vf[h][db], pb, o[db]);
       }
     }
   };
 
-  // ---- prologue: tiles 0 .. kStages-2 in flight, tile 0 landed, S^T of tile 0
-  f32x16 sA[2], sB[2];
-  int cA[2] = {0, 0}, cB[2] = {0, 0};
-  if (ntot > 0) {
+  if constexpr (!LoopCfg<D>::kPipelined) {
+    // ---- one tile at a time: tile t+kStages-1 is loaded while tile t is computed.
+    //      Tiles [0, nf) are full for every row of the workgroup (keys of blocks before
+    //      the first row's block) and skip classification and masks.
 #pragma unroll
     for (int i = 0; i < kStages - 1; ++i)
       if (i < ntot) issue(i);
-    const int after0 = min(kStages - 2, ntot - 1);  // tiles issued after tile 0
-    if (after0 >= 2) wait_vmem<2 * NIW>();
-    else if (after0 == 1) wait_vmem<NIW>();
-    else wait_vmem<0>();
-    __syncthreads();
-    classify_tile(0, cA);
-    qk(0, cA, sA);
-  }
-
-  // ---- main loop, unrolled by two so the score buffers alternate without copies
-  auto step = [&](int t, int (&cc)[2], f32x16 (&scur)[2], int (&cn)[2], f32x16 (&snext)[2]) {
-    if (t + 1 < ntot) {
-      // tile t+1 must have landed; tiles issued after it may stay in flight
-      if (t + 2 < ntot) wait_vmem<NIW>();
+    const Interval cm = common_interval(kind, 0, q0, r_last, S, L, 0);
+    const int nf = max(0, min(min(cm.hi / kBN, tr0.last) - tr0.first, n0));
+    for (int t = 0; t < ntot; ++t) {
+      if (t + 1 < ntot) wait_vmem<NIW>();  // tile t landed; tile t+1 may be in flight
       else wait_vmem<0>();
+      __syncthreads();  // everyone is done with tile t-1; its stage is free
+      if (t + kStages - 1 < ntot) issue(t + kStages - 1);
+      int cls[2];
+      if (t < nf) {
+        cls[0] = cls[1] = wave_live ? 2 : 0;
+      } else {
+        classify_tile(t, cls);
+      }
+      if (!cls[0] && !cls[1]) continue;
+      f32x16 sc[2];
+      qk(t, cls, sc);
+      softmax_pv(t, cls, sc);
     }
-    __syncthreads();  // everyone is done with tile t-1; its stage is free
-    if (t + kStages - 1 < ntot) issue(t + kStages - 1);
-    if (t + 1 < ntot) {
-      classify_tile(t + 1, cn);
-      qk(t + 1, cn, snext);
+  } else {
+  // ---- prologue: tiles 0 .. kStages-2 in flight, tile 0 landed, S^T of tile 0
+    f32x16 sA[2], sB[2];
+    int cA[2] = {0, 0}, cB[2] = {0, 0};
+    if (ntot > 0) {
+  #pragma unroll
+      for (int i = 0; i < kStages - 1; ++i)
+        if (i < ntot) issue(i);
+      const int after0 = min(kStages - 2, ntot - 1);  // tiles issued after tile 0
+      if (after0 >= 2) wait_vmem<2 * NIW>();
+      else if (after0 == 1) wait_vmem<NIW>();
+      else wait_vmem<0>();
+      __syncthreads();
+      classify_tile(0, cA);
+      qk(0, cA, sA);
     }
-    softmax_pv(t, cc, scur);
-  };
-  int t = 0;
-  for (; t + 1 < ntot; t += 2) {
-    step(t, cA, sA, cB, sB);
-    step(t + 1, cB, sB, cA, sA);
+  
+    // ---- main loop.  Tiles [0, nf) are full for every row of the workgroup (they hold
+    //      keys of blocks strictly before the first row's block), so they take a
+    //      branch-free path with no classification and no mask.  The loop is unrolled
+    //      by two so the score buffers alternate without copies.
+    int nf = 0;
+    {
+      const Interval cm = common_interval(kind, 0, q0, r_last, S, L, 0);
+      nf = min(cm.hi / kBN, tr0.last) - tr0.first;  // whole tiles inside [0, common hi)
+      nf = max(0, min(nf, n0));
+    }
+    auto sync_and_issue = [&](int t) {
+      if (t + 1 < ntot) {
+        // tile t+1 must have landed; tiles issued after it may stay in flight
+        if (t + 2 < ntot) wait_vmem<NIW>();
+        else wait_vmem<0>();
+      }
+      __syncthreads();  // everyone is done with tile t-1; its stage is free
+      if (t + kStages - 1 < ntot) issue(t + kStages - 1);
+    };
+    // Full tile t (and full tile t+1): S^T(t+1) on the MFMA beside softmax(t), then PV(t).
+    auto fast_step = [&](int t, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+      sync_and_issue(t);
+      if (!wave_live) return;
+      qk_blocks<D, 2>(lds0 + 2u * (uint32_t)(((t + 1) % kStages) * STAGE), koff, qf, snext, 3);
+      const uint32_t vb = lds0 + 2u * (uint32_t)((t % kStages) * STAGE + TILE);
+      float mx = scur[0][0];
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scur[kb][j]);
+      const float rmax = pair_max(mx);
+      const bool need = rmax * c > ms + kLazy;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        if (need) {
+          const float m_new = rmax * c;
+          const float alpha = fast_exp2(ms - m_new);
+          l *= alpha;
+  #pragma unroll
+          for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+          ms = m_new;
+        }
+      }
+      float rs = 0.f;
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float e = fast_exp2(fmaf(scur[kb][j], c, -ms));
+          scur[kb][j] = e;
+          rs += e;
+        }
+      }
+      l += rs;
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 vf[2][NDB];
+        read_vt_tile32<D>(vb + (uint32_t)(kb * 64 * D), offA, offB, vf);
+  #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j0 = h * 8;
+          const bf16x8 pb = to_bf16x8(scur[kb][j0], scur[kb][j0 + 1], scur[kb][j0 + 2],
+                                      scur[kb][j0 + 3], scur[kb][j0 + 4], scur[kb][j0 + 5],
+                                      scur[kb][j0 + 6], scur[kb][j0 + 7]);
+  #pragma unroll
+          for (int db = 0; db < NDB; ++db) o[db] = mfma32(vf[h][db], pb, o[db]);
+        }
+      }
+    };
+    // Any tile: classification, masks and skips.
+    auto step = [&](int t, int (&cc)[2], f32x16 (&scur)[2], int (&cn)[2], f32x16 (&snext)[2]) {
+      sync_and_issue(t);
+      if (t + 1 < ntot) {
+        classify_tile(t + 1, cn);
+        qk(t + 1, cn, snext);
+      }
+      softmax_pv(t, cc, scur);
+    };
+    int t = 0;
+    // fast region: steps t with t + 1 < nf (tiles t and t+1 both full)
+    for (; t + 2 < nf; t += 2) {
+      fast_step(t, sA, sB);
+      fast_step(t + 1, sB, sA);
+    }
+    if (t + 1 < nf) {
+      fast_step(t, sA, sB);
+      ++t;
+      // tile t's scores are now in sB: continue the general loop from there
+      cB[0] = cB[1] = wave_live ? 2 : 0;
+      for (; t + 1 < ntot; t += 2) {
+        step(t, cB, sB, cA, sA);
+        step(t + 1, cA, sA, cB, sB);
+      }
+      if (t < ntot) step(t, cB, sB, cA, sA);
+    } else {
+      if (t > 0) cA[0] = cA[1] = wave_live ? 2 : 0;  // tile t < nf is full
+      for (; t + 1 < ntot; t += 2) {
+        step(t, cA, sA, cB, sB);
+        step(t + 1, cB, sB, cA, sA);
+      }
+      if (t < ntot) step(t, cA, sA, cB, sB);
+    }
+  
   }
-  if (t < ntot) step(t, cA, sA, cB, sB);
 
   // ---- epilogue
-  const float l_tot = l + __shfl_xor(l, 32);
+  const float l_tot = pair_sum(l);
   if (row_ok) {
     const float inv = 1.f / l_tot;
     __bf16* orow = p.o[slot] + q_off + (size_t)qi * D;
@@ -427,7 +539,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
 
 template <int D>
 hipError_t launch_train_bf16_d(const TrainParams& p, int grid, hipStream_t stream) {
-  const size_t smem = (size_t)kStages * Geo<D>::STAGE * sizeof(__bf16);
+  const size_t smem = (size_t)LoopCfg<D>::kStages * Geo<D>::STAGE * sizeof(__bf16);
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)train_fwd_bf16_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

@@ -43,6 +43,20 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum of x over the lane pair (l, l ^ 32), which hold the two halves of one query
+// row in the 32x32 accumulator layout.  v_permlane32_swap gives every lane the values
+// of lanes l % 32 and l % 32 + 32 (checked on gfx950), combined in that fixed order.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wave-uniform value (moves it to a scalar register).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -254,6 +268,89 @@ __device__ __forceinline__ void tr_reads(const uint32_t (&a)[8], long (&o)[16]) 
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
         "v"(a[7]), "i"(OFF)
       : "memory");
+}
+
+// Batched 16-byte LDS reads (the K operands of S^T = K Q^T), in one asm block that
+// waits for them, so one LDS round trip covers a whole batch of MFMAs instead of one
+// each.  kreadN<OFF>: o[i] = 16 bytes at a[i] + OFF.
+template <int OFF>
+__device__ __forceinline__ void kread8(const uint32_t (&a)[8], bf16x8 (&o)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%16\n\t"
+      "ds_read_b128 %1, %9 offset:%16\n\t"
+      "ds_read_b128 %2, %10 offset:%16\n\t"
+      "ds_read_b128 %3, %11 offset:%16\n\t"
+      "ds_read_b128 %4, %12 offset:%16\n\t"
+      "ds_read_b128 %5, %13 offset:%16\n\t"
+      "ds_read_b128 %6, %14 offset:%16\n\t"
+      "ds_read_b128 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+        "v"(a[7]), "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void kread4(const uint32_t (&a)[4], bf16x8 (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void kread2(const uint32_t (&a)[2], bf16x8 (&o)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%4\n\t"
+      "ds_read_b128 %1, %3 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1])
+      : "v"(a[0]), "v"(a[1]), "i"(OFF)
+      : "memory");
+}
+
+// S^T = K Q^T for the 32-key blocks of a K tile at LDS byte address kbase whose mask
+// `want` is set (bit kb = block kb; NB blocks of 32 keys, 64*D bytes apart).  The K
+// operands of a block are read in one batch, then its MFMAs issue back to back; the
+// next block's reads overlap the previous block's MFMAs.
+template <int D, int KB>
+__device__ __forceinline__ void kread_block(uint32_t kbase, const uint32_t (&koff)[D / 16],
+                                            bf16x8 (&kf)[D / 16]) {
+  constexpr int NC = D / 16;
+  uint32_t a[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) a[cc] = kbase + koff[cc];
+  if constexpr (NC == 8) kread8<KB * 64 * D>(a, kf);
+  else if constexpr (NC == 4) kread4<KB * 64 * D>(a, kf);
+  else kread2<KB * 64 * D>(a, kf);
+}
+template <int D, int NB>
+__device__ __forceinline__ void qk_blocks(uint32_t kbase, const uint32_t (&koff)[D / 16],
+                                          const bf16x8 (&qf)[D / 16], f32x16 (&sc)[NB],
+                                          int want) {
+  constexpr int NC = D / 16;
+  bf16x8 kf[NC];
+  if (want & 1) {
+    kread_block<D, 0>(kbase, koff, kf);
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) acc = mfma32(kf[cc], qf[cc], acc);
+    sc[0] = acc;
+  }
+  if constexpr (NB > 1) {
+    if (want & 2) {
+      kread_block<D, 1>(kbase, koff, kf);
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) acc = mfma32(kf[cc], qf[cc], acc);
+      sc[1] = acc;
+    }
+  }
 }
 
 __device__ __forceinline__ bf16x8 join_bf16(long lo, long hi) {
