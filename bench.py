@@ -64,19 +64,40 @@ def pairs_blockcausal(L: int, S: int) -> int:
 
 
 def timed_launches(fn, n, stream):
-    """Run fn() n times with HIP events around every launch on ``stream``; returns
-    (total ms from the first start to the last end, mean per-launch ms)."""
+    """Run fn() n times back to back between two HIP events recorded on ``stream`` (the
+    stream the kernels run on), with a synchronisation on both sides; returns (total ms,
+    mean ms per launch)."""
     import torch
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    for i in range(n):
-        starts[i].record(stream)
-        fn()
-        ends[i].record(stream)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    per = [starts[i].elapsed_time(ends[i]) for i in range(n)]
-    return starts[0].elapsed_time(ends[-1]), sum(per) / n
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    return total, total / n
+
+
+def graph_of(fn, n):
+    """A HIP graph holding n back-to-back calls of fn (kernel launches on the current
+    stream), so timed replays measure the GPU and not the Python launch overhead."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up launch outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return g
 
 
 def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True):
@@ -102,14 +123,21 @@ def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True):
         m.e2d2_attn_train_fwd(qd, kc, vc, kd, vd, od, S, lse_dec=ld, q_enc=qe, o_enc=oe,
                               lse_enc=le)
 
-    stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    ref = (od.clone(), oe.clone())
+    # the timed region: `steps` launches replayed from one HIP graph, bracketed by HIP
+    # events on the stream they run on
+    g = graph_of(step, steps)
+    g.replay()  # untimed: part of the warm-up
+    stream = torch.cuda.current_stream(dev)
     t0 = time.perf_counter()
-    total_ms, kern_ms = timed_launches(step, steps, stream)
+    total_ms, kern_ms = timed_launches(g.replay, 1, stream)
+    kern_ms = total_ms / steps
     wall = time.perf_counter() - t0
-    torch.cuda.synchronize()
+    if not (torch.equal(od, ref[0]) and torch.equal(oe, ref[1])):
+        raise RuntimeError("graph replay differs from the eager launch")
     useful = 4.0 * d * 2 * pairs_blockcausal(L, S) * B * Hq
     return dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=kern_ms,
                 useful_flop=useful, wall_s=wall)
@@ -155,11 +183,20 @@ def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
             step(t)
         append()
     torch.cuda.synchronize()
+    # warm: the T steps of a block back to back from one HIP graph (as a decode loop
+    # runs them), then the append, each bracketed by HIP events on the launch stream
+    it = [0]
+
+    def next_step():
+        step(it[0] % T)
+        it[0] += 1
+
+    g = graph_of(next_step, T)
+    g.replay()  # untimed warm-up
     step_ms, append_ms = [], []
     for _ in range(blocks):
-        for t in range(T):
-            _, ms = timed_launches(lambda: step(t), 1, stream)
-            step_ms.append(ms)
+        _, ms = timed_launches(g.replay, 1, stream)
+        step_ms.append(ms / T)
         _, ms = timed_launches(append, 1, stream)
         append_ms.append(ms)
     # cold: before each step, sweep a 1 GiB buffer with reads only, so the 256 MB
@@ -187,7 +224,7 @@ def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
         us_per_step_warm=warm * 1e3, us_per_step_cold=cold * 1e3,
         us_per_step_mean_warm=sum(step_ms) / len(step_ms) * 1e3,
         gbs_warm=alg / (warm * 1e-3) / 1e9, gbs_cold=alg / (cold * 1e-3) / 1e9,
-        algorithmic_bytes_per_step=alg, steps_timed=len(step_ms),
+        algorithmic_bytes_per_step=alg, steps_timed=len(step_ms) * T,
         append_us=app * 1e3, append_gbs=app_bytes / (app * 1e-3) / 1e9,
         roofline=dict(bound="hbm", achieved=round(alg / (cold * 1e-3) / 1e9, 1),
                       peak=PEAK_HBM_GBS, unit="GB/s",

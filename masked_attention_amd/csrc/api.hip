@@ -36,7 +36,7 @@ e2d2_status check_train_shape(int dtype, int B, int Hq, int Hkv, int L, int d, i
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || S <= 0) return E2D2_ERR_SHAPE;
   if (Hq % Hkv != 0 || L > kMaxLen || !scale_ok(scale)) return E2D2_ERR_SHAPE;
   if (!slice_ok(L, d)) return E2D2_ERR_SHAPE;
-  const int bm = dtype == E2D2_BF16 ? e2d2::train_tile_bm() : e2d2::kF32TileBM;
+  const int bm = dtype == E2D2_BF16 ? e2d2::train_tile_bm(d) : e2d2::kF32TileBM;
   if ((long long)B * Hq * 2 * cdiv(L, bm) > INT32_MAX) return E2D2_ERR_SHAPE;
   return E2D2_OK;
 }
@@ -122,7 +122,7 @@ e2d2_status e2d2_attn_encoder_blockcausal(int dtype, int B, int Hq, int Hkv, int
     p.kinds[0] = p.kinds[1] = e2d2::kEnc;
     p.n_kinds = 1;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
-    p.n_qtiles = cdiv(L, e2d2::train_tile_bm());
+    p.n_qtiles = cdiv(L, e2d2::train_tile_bm(d));
     p.xcd_groups = (B * Hq) % 8 == 0;
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
@@ -176,7 +176,7 @@ e2d2_status e2d2_attn_train_fwd(int dtype, int B, int Hq, int Hkv, int L, int d,
     p.kinds[1] = e2d2::kEnc;
     p.n_kinds = with_enc ? 2 : 1;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
-    p.n_qtiles = cdiv(L, e2d2::train_tile_bm());
+    p.n_qtiles = cdiv(L, e2d2::train_tile_bm(d));
     p.xcd_groups = (B * Hq * p.n_kinds) % 8 == 0;
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
@@ -310,7 +310,7 @@ e2d2_status e2d2_attn_tile_shape(int kind, int dtype, int d, int* bm, int* bn) {
   if (!bm || !bn) return E2D2_ERR_NULL;
   if ((dtype != E2D2_F32 && dtype != E2D2_BF16) || !head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
   if (kind == E2D2_KIND_ENC || kind == E2D2_KIND_DEC) {
-    *bm = dtype == E2D2_BF16 ? e2d2::train_tile_bm() : e2d2::kF32TileBM;
+    *bm = dtype == E2D2_BF16 ? e2d2::train_tile_bm(d) : e2d2::kF32TileBM;
     *bn = dtype == E2D2_BF16 ? e2d2::train_tile_bn() : e2d2::kF32TileBN;
     return E2D2_OK;
   }

@@ -40,21 +40,29 @@
 namespace e2d2 {
 namespace {
 
-constexpr int kBM = 128;
-constexpr int kBN = 64;
-constexpr int kWaves = 4;
-// Loop structure per head dimension (measured on MI355X): at d <= 64 the registers of a
-// simple tile-at-a-time loop allow 3 waves per SIMD (3-deep LDS ring), whose interleaving
-// overlaps one wave's softmax with another's MFMAs; at d = 128 the accumulators allow a
-// single wave per SIMD, so the loop is software-pipelined instead (4-deep ring).
+constexpr int kBN = 64;           // keys per tile
+constexpr float kLazy = 8.f;      // rescale only when a row max grows by > 2^8
+constexpr float kNegBig = -1e30f; // "no key yet" running max (finite: no inf - inf)
+
+// Loop structure per head dimension (measured on MI355X).  LDS bounds the design:
+// workgroups per CU x ring depth x tile bytes must fit in 160 KiB.
+//   d <= 64: a tile-at-a-time loop light enough for 4 waves per SIMD; 128 query rows
+//     (4 waves) per workgroup and a 2-deep ring (32 KiB at d = 64), so four workgroups
+//     share a CU and one wave's softmax overlaps another's MFMAs.  (Measured faster than
+//     256-row workgroups with a 4-deep ring at two per CU: 55.5 vs 64.8 us on the
+//     B8 H16 L1024 S16 training forward.)
+//   d = 128: the accumulators allow one wave per SIMD, so the loop is software-
+//     pipelined instead (S^T of tile t+1 beside the softmax of tile t), 128 rows, 4-deep
+//     ring.
 template <int D>
 struct LoopCfg {
   static constexpr bool kPipelined = D > 64;
-  static constexpr int kStages = D > 64 ? 4 : 3;
-  static constexpr int kOccupancy = D > 64 ? 1 : 3;
+  static constexpr int kBM = 128;
+  static constexpr int kWaves = kBM / 32;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kStages = D > 64 ? 4 : 2;
+  static constexpr int kBlocksPerCU = D > 64 ? 1 : 4;
 };
-constexpr float kLazy = 8.f;      // rescale only when a row max grows by > 2^8
-constexpr float kNegBig = -1e30f; // "no key yet" running max (finite: no inf - inf)
 
 template <int D>
 struct Geo {
@@ -62,13 +70,15 @@ struct Geo {
   static constexpr int NDB = D / 32;  // 32-wide head-dim blocks of O^T
   static constexpr int TILE = kBN * D;  // bf16 elements of one K or V tile
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int NIW = 2 * (kBN * (D / 8) / 64) / kWaves;  // loads per wave per tile
+  static constexpr int NIW = 2 * (kBN * (D / 8) / 64) / LoopCfg<D>::kWaves;  // loads per wave per tile
 };
 
 template <int D>
-__global__ __launch_bounds__(256, LoopCfg<D>::kOccupancy) void train_fwd_bf16_kernel(TrainParams p) {
+__global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) void train_fwd_bf16_kernel(TrainParams p) {
   using G = Geo<D>;
   constexpr int kStages = LoopCfg<D>::kStages;
+  constexpr int kBM = LoopCfg<D>::kBM;
+  constexpr int kWaves = LoopCfg<D>::kWaves;
   constexpr int NC = G::NC, NDB = G::NDB, TILE = G::TILE, STAGE = G::STAGE, NIW = G::NIW;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
 
@@ -545,7 +555,7 @@ hipError_t launch_train_bf16_d(const TrainParams& p, int grid, hipStream_t strea
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(train_fwd_bf16_kernel<D>, dim3(grid), dim3(256), smem, stream, p);
+  hipLaunchKernelGGL(train_fwd_bf16_kernel<D>, dim3(grid), dim3(LoopCfg<D>::kThreads), smem, stream, p);
   return hipGetLastError();
 }
 
@@ -557,7 +567,9 @@ hipError_t launch_f32_d(const F32Params& p, int grid, hipStream_t stream) {
 
 }  // namespace
 
-int train_tile_bm() { return kBM; }
+int train_tile_bm(int d) {
+  return d == 64 ? LoopCfg<64>::kBM : (d == 32 ? LoopCfg<32>::kBM : LoopCfg<128>::kBM);
+}
 int train_tile_bn() { return kBN; }
 
 hipError_t launch_train_bf16(const TrainParams& p, int d, hipStream_t stream) {

@@ -66,7 +66,7 @@ struct DenoiseParams {
   unsigned long long* visits;
 };
 
-int train_tile_bm();
+int train_tile_bm(int d);
 int train_tile_bn();
 constexpr int kF32TileBM = 64;
 constexpr int kF32TileBN = 64;
