@@ -81,6 +81,22 @@ def timed_launches(fn, n, stream):
     return total, total / n
 
 
+def clock_warmup(replay, min_ms=150.0):
+    """Keep the GPU busy for at least min_ms with back-to-back replays right before a
+    timed region: the MI355X raises its clocks over the first ~50 ms of sustained work
+    and lowers them again after idling, so a cold start would time the ramp."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    replay()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-5) * 1e3
+    for _ in range(int(min_ms / one) + 1):
+        replay()
+    torch.cuda.synchronize()
+
+
 def graph_of(fn, n):
     """A HIP graph holding n back-to-back calls of fn (kernel launches on the current
     stream), so timed replays measure the GPU and not the Python launch overhead."""
@@ -123,14 +139,16 @@ def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True):
         m.e2d2_attn_train_fwd(qd, kc, vc, kd, vd, od, S, lse_dec=ld, q_enc=qe, o_enc=oe,
                               lse_enc=le)
 
-    for _ in range(warmup):
-        step()
+    step()
     torch.cuda.synchronize()
     ref = (od.clone(), oe.clone())
     # the timed region: `steps` launches replayed from one HIP graph, bracketed by HIP
-    # events on the stream they run on
+    # events on the stream they run on.  Warm-up: `warmup` launches (eager and replayed),
+    # and at least 150 ms of replays just before the timed one.
     g = graph_of(step, steps)
-    g.replay()  # untimed: part of the warm-up
+    for _ in range(max(1, -(-warmup // steps))):
+        g.replay()
+    clock_warmup(g.replay)
     stream = torch.cuda.current_stream(dev)
     t0 = time.perf_counter()
     total_ms, kern_ms = timed_launches(g.replay, 1, stream)
@@ -193,22 +211,41 @@ def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
 
     g = graph_of(next_step, T)
     g.replay()  # untimed warm-up
+    clock_warmup(g.replay)
     step_ms, append_ms = [], []
     for _ in range(blocks):
         _, ms = timed_launches(g.replay, 1, stream)
         step_ms.append(ms / T)
-        _, ms = timed_launches(append, 1, stream)
-        append_ms.append(ms)
+        # the append is timed behind a replay still running on the GPU, so its events
+        # bracket the kernel rather than the host's launch path
+        torch.cuda.synchronize()
+        g.replay()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        append()
+        end.record(stream)
+        torch.cuda.synchronize()
+        append_ms.append(start.elapsed_time(end))
     # cold: before each step, sweep a 1 GiB buffer with reads only, so the 256 MB
     # Infinity Cache and the L2 hold other, clean lines (a write sweep would leave dirty
     # lines whose write-back would be charged to the step)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
+    clock_warmup(g.replay)
+    # The flush keeps the GPU busy for a few hundred us, far longer than the host needs to
+    # record the start event and launch the step, so the step starts right after the
+    # event and the pair times the kernel, not the launch path of one isolated call.
     cold_ms = []
     for t in range(min(T, 16)):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         flush.sum()
-        _, ms = timed_launches(lambda: step(t), 1, stream)
-        cold_ms.append(ms)
+        start.record(stream)
+        step(t)
+        end.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(start.elapsed_time(end))
     del flush
     cache_bytes = 2 * B * Hkv * C * d * 2
     blk_bytes = 2 * B * Hkv * S * d * 2
@@ -270,8 +307,8 @@ def cpu_baseline(budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", choices=["all", "train", "denoise", "long", "copycal"],
                     default="all",
                     help="restrict the run (profiling); 'copycal' runs only a plain 1 GiB "

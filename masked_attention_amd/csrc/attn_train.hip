@@ -41,7 +41,7 @@ namespace e2d2 {
 namespace {
 
 constexpr int kBN = 64;           // keys per tile
-constexpr float kLazy = 8.f;      // rescale only when a row max grows by > 2^8
+constexpr float kBound = 65536.f; // lane sum of a tile's numerators that forces a rescale
 constexpr float kNegBig = -1e30f; // "no key yet" running max (finite: no inf - inf)
 
 // Loop structure per head dimension (measured on MI355X).  LDS bounds the design:
@@ -142,6 +142,13 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     }
   };
 
+  if constexpr (!LoopCfg<D>::kPipelined) {
+    // first tiles in flight before the per-row setup below
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < ntot) issue(i);
+  }
+
   // ---- per-wave rows and per-lane query row
   const int wq0 = q0 + wave * 32;
   const bool wave_live = wq0 < L;
@@ -217,11 +224,10 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     const int want = (cls[0] ? 1 : 0) | (cls[1] ? 2 : 0);
     if (want) qk_blocks<D, 2>(lds0 + 2u * (uint32_t)((t % kStages) * STAGE), koff, qf, sc, want);
   };
-  // Mask, online softmax (lazy rescale), P in bf16, then O^T += V^T P^T for tile t.
-  auto softmax_pv = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
+  // Element mask of the partly allowed blocks of tile t.
+  auto mask = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
     const int src = tsrc(t);
     const int kt0 = tnum(t) * kBN;
-    const uint32_t vb = lds0 + 2u * (uint32_t)((t % kStages) * STAGE + TILE);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (cls[kb] == 1) {
@@ -233,18 +239,28 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
         }
       }
     }
-    float mx = -INFINITY;
+  };
+  // Numerators of tile t against the running max (online softmax, base 2), packed to
+  // bf16; returns the lane's sum of them.  Rescaling is lazy and needs no row max on
+  // the common path: when a lane's sum exceeds kBound (the row's first keys, or scores
+  // that outgrew the running max), the row takes its max over the tile, rescales O and
+  // l, and the tile's numerators are formed again.  The decision is per row (the lane
+  // pair), so a row's arithmetic depends on its own keys only.
+  auto softmax = [&](const int (&cls)[2], const f32x16 (&sc)[2], bf16x8 (&pb)[2][2]) {
+    float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      if (cls[kb]) {
+      if (cls[kb]) rs = exp_pack(sc[kb], c, -ms, pb[kb], rs);
+    if (__builtin_amdgcn_ballot_w64(rs > kBound) != 0) {
+      float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
-      }
-    // Per-row decision (both lanes of a row see the row max), so a row's arithmetic
-    // depends only on its own allowed keys.
-    const float rmax = pair_max(mx);
-    const bool need = rmax * c > ms + kLazy;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      for (int kb = 0; kb < 2; ++kb)
+        if (cls[kb]) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
+        }
+      const float rmax = pair_max(mx);
+      const bool need = pair_max(rs > kBound ? 1.f : 0.f) > 0.f;
       if (need) {
         const float m_new = rmax * c;
         const float alpha = fast_exp2(ms - m_new);
@@ -255,44 +271,47 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
           for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
         ms = m_new;
       }
+      rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (cls[kb]) rs = exp_pack(sc[kb], c, -ms, pb[kb], rs);
     }
+    l += rs;
+  };
+  // O^T += V^T P^T for the allowed blocks of the tile in stage `stage`.
+  auto pv = [&](int stage, const int (&cls)[2], const bf16x8 (&pb)[2][2]) {
+    const uint32_t vb = lds0 + 2u * (uint32_t)(stage * STAGE + TILE);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!cls[kb]) continue;
-      float rs = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(fmaf(sc[kb][j], c, -ms));
-        sc[kb][j] = e;
-        rs += e;
-      }
-      l += rs;
-      bf16x8 vf[2][NDB];
-      read_vt_tile32<D>(vb + (uint32_t)(kb * 64 * D), offA, offB, vf);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j0 = h * 8;
-        const bf16x8 pb = to_bf16x8(sc[kb][j0], sc[kb][j0 + 1], sc[kb][j0 + 2], sc[kb][j0 + 3],
-                                    sc[kb][j0 + 4], sc[kb][j0 + 5], sc[kb][j0 + 6], sc[kb][j0 + 7]);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] = mfma32(vf[h][db], pb, o[db]);
-      }
-    }
+    for (int kb = 0; kb < 2; ++kb)
+      if (cls[kb]) pv_block<D, 0>(vb + (uint32_t)(kb * 64 * D), offA, offB, pb[kb], o);
   };
 
   if constexpr (!LoopCfg<D>::kPipelined) {
-    // ---- one tile at a time: tile t+kStages-1 is loaded while tile t is computed.
-    //      Tiles [0, nf) are full for every row of the workgroup (keys of blocks before
-    //      the first row's block) and skip classification and masks.
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
-      if (i < ntot) issue(i);
+    // ---- one tile at a time through a kStages-deep ring: tiles t+1 .. t+kStages-1 are
+    //      in flight while tile t is computed.  Unrolled by kStages so the stage of each
+    //      tile is a constant that the LDS reads carry in their offset field.  Tiles
+    //      [0, nf) are full for every row of the workgroup (keys of blocks before the
+    //      first row's block) and skip classification and masks.
+    static_assert(kStages >= 2 && kStages <= 4, "unrolled for 2..4 stages");
     const Interval cm = common_interval(kind, 0, q0, r_last, S, L, 0);
     const int nf = max(0, min(min(cm.hi / kBN, tr0.last) - tr0.first, n0));
-    for (int t = 0; t < ntot; ++t) {
-      if (t + 1 < ntot) wait_vmem<NIW>();  // tile t landed; tile t+1 may be in flight
-      else wait_vmem<0>();
-      __syncthreads();  // everyone is done with tile t-1; its stage is free
+    auto tile = [&](int t, auto stg) {
+      constexpr int KOFF = decltype(stg)::value * STAGE * 2;
+      constexpr int VOFF = KOFF + TILE * 2;
+      // Tile t must have landed; the tiles issued after it (up to kStages - 2 of them)
+      // may stay in flight.  The barrier then makes every wave's part of tile t visible
+      // and frees the stage of tile t-1 for tile t+kStages-1.
+      if constexpr (kStages >= 4) {
+        if (t + 2 < ntot) wait_vmem<2 * NIW>();
+        else if (t + 1 < ntot) wait_vmem<NIW>();
+        else wait_vmem<0>();
+      } else if constexpr (kStages == 3) {
+        if (t + 1 < ntot) wait_vmem<NIW>();
+        else wait_vmem<0>();
+      } else {
+        wait_vmem<0>();
+      }
+      __syncthreads();
       if (t + kStages - 1 < ntot) issue(t + kStages - 1);
       int cls[2];
       if (t < nf) {
@@ -300,10 +319,25 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       } else {
         classify_tile(t, cls);
       }
-      if (!cls[0] && !cls[1]) continue;
+      const int want = (cls[0] ? 1 : 0) | (cls[1] ? 2 : 0);
+      if (!want) return;
       f32x16 sc[2];
-      qk(t, cls, sc);
-      softmax_pv(t, cls, sc);
+      qk_blocks<D, 2, KOFF>(lds0, koff, qf, sc, want);
+      if (t >= nf) mask(t, cls, sc);
+      bf16x8 pb[2][2];
+      softmax(cls, sc, pb);
+      if (cls[0]) pv_block<D, VOFF>(lds0, offA, offB, pb[0], o);
+      if (cls[1]) pv_block<D, VOFF + 64 * D>(lds0, offA, offB, pb[1], o);
+    };
+    for (int t = 0; t < ntot; t += kStages) {
+      tile(t, IntC<0>{});
+      if (t + 1 < ntot) tile(t + 1, IntC<1>{});
+      if constexpr (kStages > 2) {
+        if (t + 2 < ntot) tile(t + 2, IntC<2 % kStages>{});
+      }
+      if constexpr (kStages > 3) {
+        if (t + 3 < ntot) tile(t + 3, IntC<3 % kStages>{});
+      }
     }
   } else {
   // ---- prologue: tiles 0 .. kStages-2 in flight, tile 0 landed, S^T of tile 0
@@ -313,6 +347,7 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   #pragma unroll
       for (int i = 0; i < kStages - 1; ++i)
         if (i < ntot) issue(i);
+      static_assert(kStages >= 3 && kStages <= 4, "S^T of tile t+1 is formed during step t");
       const int after0 = min(kStages - 2, ntot - 1);  // tiles issued after tile 0
       if (after0 >= 2) wait_vmem<2 * NIW>();
       else if (after0 == 1) wait_vmem<NIW>();
@@ -321,7 +356,7 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       classify_tile(0, cA);
       qk(0, cA, sA);
     }
-  
+
     // ---- main loop.  Tiles [0, nf) are full for every row of the workgroup (they hold
     //      keys of blocks strictly before the first row's block), so they take a
     //      branch-free path with no classification and no mask.  The loop is unrolled
@@ -334,8 +369,9 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     }
     auto sync_and_issue = [&](int t) {
       if (t + 1 < ntot) {
-        // tile t+1 must have landed; tiles issued after it may stay in flight
-        if (t + 2 < ntot) wait_vmem<NIW>();
+        // tile t+1 must have landed; the tiles issued after it (t+2 .. t+kStages-2)
+        // may stay in flight
+        if (kStages >= 4 && t + 2 < ntot) wait_vmem<(kStages - 3) * NIW>();
         else wait_vmem<0>();
       }
       __syncthreads();  // everyone is done with tile t-1; its stage is free
@@ -346,51 +382,10 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       sync_and_issue(t);
       if (!wave_live) return;
       qk_blocks<D, 2>(lds0 + 2u * (uint32_t)(((t + 1) % kStages) * STAGE), koff, qf, snext, 3);
-      const uint32_t vb = lds0 + 2u * (uint32_t)((t % kStages) * STAGE + TILE);
-      float mx = scur[0][0];
-  #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scur[kb][j]);
-      const float rmax = pair_max(mx);
-      const bool need = rmax * c > ms + kLazy;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        if (need) {
-          const float m_new = rmax * c;
-          const float alpha = fast_exp2(ms - m_new);
-          l *= alpha;
-  #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-  #pragma unroll
-            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-          ms = m_new;
-        }
-      }
-      float rs = 0.f;
-  #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-  #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = fast_exp2(fmaf(scur[kb][j], c, -ms));
-          scur[kb][j] = e;
-          rs += e;
-        }
-      }
-      l += rs;
-  #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 vf[2][NDB];
-        read_vt_tile32<D>(vb + (uint32_t)(kb * 64 * D), offA, offB, vf);
-  #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int j0 = h * 8;
-          const bf16x8 pb = to_bf16x8(scur[kb][j0], scur[kb][j0 + 1], scur[kb][j0 + 2],
-                                      scur[kb][j0 + 3], scur[kb][j0 + 4], scur[kb][j0 + 5],
-                                      scur[kb][j0 + 6], scur[kb][j0 + 7]);
-  #pragma unroll
-          for (int db = 0; db < NDB; ++db) o[db] = mfma32(vf[h][db], pb, o[db]);
-        }
-      }
+      const int all[2] = {2, 2};
+      bf16x8 pb[2][2];
+      softmax(all, scur, pb);
+      pv(t % kStages, all, pb);
     };
     // Any tile: classification, masks and skips.
     auto step = [&](int t, int (&cc)[2], f32x16 (&scur)[2], int (&cn)[2], f32x16 (&snext)[2]) {
@@ -399,7 +394,11 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
         classify_tile(t + 1, cn);
         qk(t + 1, cn, snext);
       }
-      softmax_pv(t, cc, scur);
+      if (!cc[0] && !cc[1]) return;
+      mask(t, cc, scur);
+      bf16x8 pb[2][2];
+      softmax(cc, scur, pb);
+      pv(t % kStages, cc, pb);
     };
     int t = 0;
     // fast region: steps t with t + 1 < nf (tiles t and t+1 both full)
@@ -425,7 +424,6 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       }
       if (t < ntot) step(t, cA, sA, cB, sB);
     }
-  
   }
 
   // ---- epilogue

@@ -22,6 +22,8 @@ namespace e2d2 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -67,6 +69,30 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
   r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
   r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
   return r;
+}
+
+// Softmax numerators of one 32-key block of S^T: p = 2^(s * c + negm) for the lane's
+// 16 scores, packed to bf16 as the two B operands of O^T += V^T P^T (pb[h] holds
+// registers 8h .. 8h+7).  Returns acc plus the sum of the packed values (v_dot2 with
+// ones, two per instruction), so the denominator adds exactly the rounded p's that the
+// numerator multiplies.
+__device__ __forceinline__ float exp_pack(const f32x16& s, float c, float negm, bf16x8 (&pb)[2],
+                                          float acc) {
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(s[8 * h + j], c, negm));
+    const bf16x8 v = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    pb[h] = v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x2 pr = {v[2 * k], v[2 * k + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+  }
+  return acc;
 }
 
 // ---------------------------------------------------------------------------------
@@ -211,62 +237,62 @@ __device__ __forceinline__ void wait_vmem() {
 // passed a workgroup barrier where other waves loaded them.  Each asm block ends with
 // s_waitcnt lgkmcnt(0), so its outputs are valid when it completes.
 //
-// tr_reads<N, OFF>: for each of the N byte addresses a[i] (LDS), reads 8 bytes at a[i]
-// and at a[i] + OFF; o[2i] gets the first, o[2i+1] the second.
-template <int OFF>
+// tr_reads<O0, O1>: for each of the N byte addresses a[i] (LDS), reads 8 bytes at
+// a[i] + O0 and at a[i] + O1; o[2i] gets the first, o[2i+1] the second.
+template <int O0, int O1>
 __device__ __forceinline__ void tr_reads(const uint32_t (&a)[2], long (&o)[4]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %2, %5\n\t"
-      "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(a[0]), "v"(a[1]), "i"(OFF)
+      : "v"(a[0]), "v"(a[1]), "i"(O0), "i"(O1)
       : "memory");
 }
-template <int OFF>
+template <int O0, int O1>
 __device__ __forceinline__ void tr_reads(const uint32_t (&a)[4], long (&o)[8]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %2, %9\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %4, %10\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %6, %11\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
         "=&v"(o[6]), "=&v"(o[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(O0), "i"(O1)
       : "memory");
 }
-template <int OFF>
+template <int O0, int O1>
 __device__ __forceinline__ void tr_reads(const uint32_t (&a)[8], long (&o)[16]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %16 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %2, %17\n\t"
-      "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %4, %18\n\t"
-      "ds_read_b64_tr_b16 %5, %18 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %6, %19\n\t"
-      "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %8, %20\n\t"
-      "ds_read_b64_tr_b16 %9, %20 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %10, %21\n\t"
-      "ds_read_b64_tr_b16 %11, %21 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %12, %22\n\t"
-      "ds_read_b64_tr_b16 %13, %22 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %14, %23\n\t"
-      "ds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %6, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
         "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]),
         "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
-        "v"(a[7]), "i"(OFF)
+        "v"(a[7]), "i"(O0), "i"(O1)
       : "memory");
 }
 
@@ -318,25 +344,28 @@ __device__ __forceinline__ void kread2(const uint32_t (&a)[2], bf16x8 (&o)[2]) {
 // `want` is set (bit kb = block kb; NB blocks of 32 keys, 64*D bytes apart).  The K
 // operands of a block are read in one batch, then its MFMAs issue back to back; the
 // next block's reads overlap the previous block's MFMAs.
-template <int D, int KB>
+// BASE: a compile-time byte offset added to kbase through the instructions' offset field.
+template <int D, int KB, int BASE = 0>
 __device__ __forceinline__ void kread_block(uint32_t kbase, const uint32_t (&koff)[D / 16],
                                             bf16x8 (&kf)[D / 16]) {
   constexpr int NC = D / 16;
+  constexpr int OFF = BASE + KB * 64 * D;
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field is 16 bits");
   uint32_t a[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) a[cc] = kbase + koff[cc];
-  if constexpr (NC == 8) kread8<KB * 64 * D>(a, kf);
-  else if constexpr (NC == 4) kread4<KB * 64 * D>(a, kf);
-  else kread2<KB * 64 * D>(a, kf);
+  if constexpr (NC == 8) kread8<OFF>(a, kf);
+  else if constexpr (NC == 4) kread4<OFF>(a, kf);
+  else kread2<OFF>(a, kf);
 }
-template <int D, int NB>
+template <int D, int NB, int BASE = 0>
 __device__ __forceinline__ void qk_blocks(uint32_t kbase, const uint32_t (&koff)[D / 16],
                                           const bf16x8 (&qf)[D / 16], f32x16 (&sc)[NB],
                                           int want) {
   constexpr int NC = D / 16;
   bf16x8 kf[NC];
   if (want & 1) {
-    kread_block<D, 0>(kbase, koff, kf);
+    kread_block<D, 0, BASE>(kbase, koff, kf);
     f32x16 acc = zero16();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) acc = mfma32(kf[cc], qf[cc], acc);
@@ -344,7 +373,7 @@ __device__ __forceinline__ void qk_blocks(uint32_t kbase, const uint32_t (&koff)
   }
   if constexpr (NB > 1) {
     if (want & 2) {
-      kread_block<D, 1>(kbase, koff, kf);
+      kread_block<D, 1, BASE>(kbase, koff, kf);
       f32x16 acc = zero16();
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) acc = mfma32(kf[cc], qf[cc], acc);
@@ -378,7 +407,7 @@ __device__ __forceinline__ void vt_offsets(int lane, uint32_t (&offA)[D / 32],
 
 // V^T operands of a whole 64-key tile at LDS byte address vbase: vf[j][db] covers keys
 // [16j, 16j + 16) and head dims [32 db, 32 db + 32).
-template <int D>
+template <int D, int BASE = 0>
 __device__ __forceinline__ void read_vt_tile64(uint32_t vbase, const uint32_t (&offA)[D / 32],
                                                const uint32_t (&offB)[D / 32],
                                                bf16x8 (&vf)[4][D / 32]) {
@@ -388,7 +417,7 @@ __device__ __forceinline__ void read_vt_tile64(uint32_t vbase, const uint32_t (&
     const uint32_t a[4] = {vbase + offA[0], vbase + offA[0] + 2 * OFF, vbase + offB[0],
                            vbase + offB[0] + 2 * OFF};
     long o[8];
-    tr_reads<OFF>(a, o);
+    tr_reads<BASE, BASE + OFF>(a, o);
 #pragma unroll
     for (int j = 0; j < 4; ++j) vf[j][0] = join_bf16(o[j], o[4 + j]);
   } else {
@@ -399,7 +428,7 @@ __device__ __forceinline__ void read_vt_tile64(uint32_t vbase, const uint32_t (&
                              vbase + offA[dp + 1] + 2 * OFF, vbase + offB[dp + 1],
                              vbase + offB[dp + 1] + 2 * OFF};
       long o[16];
-      tr_reads<OFF>(a, o);
+      tr_reads<BASE, BASE + OFF>(a, o);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         vf[j][dp] = join_bf16(o[j], o[4 + j]);
@@ -410,22 +439,23 @@ __device__ __forceinline__ void read_vt_tile64(uint32_t vbase, const uint32_t (&
 }
 
 // V^T operands of a 32-key tile: vf[j][db] covers keys [16j, 16j + 16), j = 0, 1.
-template <int D>
+template <int D, int BASE = 0>
 __device__ __forceinline__ void read_vt_tile32(uint32_t vbase, const uint32_t (&offA)[D / 32],
                                                const uint32_t (&offB)[D / 32],
                                                bf16x8 (&vf)[2][D / 32]) {
   constexpr int NDB = D / 32;
   constexpr int OFF = 32 * D;
+  static_assert(BASE >= 0 && BASE + OFF < 65536, "LDS offset field is 16 bits");
   if constexpr (NDB == 1) {
     const uint32_t a[2] = {vbase + offA[0], vbase + offB[0]};
     long o[4];
-    tr_reads<OFF>(a, o);
+    tr_reads<BASE, BASE + OFF>(a, o);
     vf[0][0] = join_bf16(o[0], o[2]);
     vf[1][0] = join_bf16(o[1], o[3]);
   } else if constexpr (NDB == 2) {
     const uint32_t a[4] = {vbase + offA[0], vbase + offB[0], vbase + offA[1], vbase + offB[1]};
     long o[8];
-    tr_reads<OFF>(a, o);
+    tr_reads<BASE, BASE + OFF>(a, o);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       vf[0][db] = join_bf16(o[4 * db], o[4 * db + 2]);
@@ -435,7 +465,7 @@ __device__ __forceinline__ void read_vt_tile32(uint32_t vbase, const uint32_t (&
     const uint32_t a[8] = {vbase + offA[0], vbase + offB[0], vbase + offA[1], vbase + offB[1],
                            vbase + offA[2], vbase + offB[2], vbase + offA[3], vbase + offB[3]};
     long o[16];
-    tr_reads<OFF>(a, o);
+    tr_reads<BASE, BASE + OFF>(a, o);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       vf[0][db] = join_bf16(o[4 * db], o[4 * db + 2]);
@@ -443,6 +473,26 @@ __device__ __forceinline__ void read_vt_tile32(uint32_t vbase, const uint32_t (&
     }
   }
 }
+
+// O^T += V^T P^T for one 32-key block whose V rows start at LDS byte address
+// vbase + BASE; pb holds the block's P^T operands (exp_pack).
+template <int D, int BASE>
+__device__ __forceinline__ void pv_block(uint32_t vbase, const uint32_t (&offA)[D / 32],
+                                         const uint32_t (&offB)[D / 32], const bf16x8 (&pb)[2],
+                                         f32x16 (&o)[D / 32]) {
+  bf16x8 vf[2][D / 32];
+  read_vt_tile32<D, BASE>(vbase, offA, offB, vf);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = mfma32(vf[h][db], pb[h], o[db]);
+}
+
+// A compile-time int carried as a value (selects a template branch from a loop body).
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 
 // LDS byte address of an LDS pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void E2D2_LDS* p) {
