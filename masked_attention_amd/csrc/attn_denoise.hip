@@ -16,14 +16,18 @@
 //     the queries that read that kv head (grouped query heads share one K/V stream),
 //     so every cached K/V byte is read from HBM once per step.
 //   * The key axis (cache rows [0, C), then the block's own S keys) is cut into
-//     32-key tiles.  The 4 waves of a workgroup take every 4th tile and stream them
-//     independently (no barrier in the loop) through a wave-private, double-buffered
-//     LDS stage filled by buffer_load_dwordx4 ... lds, so each wave keeps one tile in
-//     flight while it computes the other.
+//     32-key tiles.  The 8 waves of a workgroup form 4 pairs; pair p takes every 4th
+//     tile (p, p + 4, ...) and streams it through its own double-buffered LDS ring
+//     filled by buffer_load_dwordx4 ... lds (each wave of the pair loads half of the
+//     tile), and each wave of the pair computes one of the two column blocks against
+//     it.  One workgroup barrier per round (all pairs step together) publishes the
+//     round's tiles and frees the other stage; the next round's tiles are in flight
+//     while the current one is computed.  One column block per wave keeps the
+//     accumulators within 256 registers, so two waves share each SIMD.
 //   * Per tile: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with an
 //     online base-2 softmax with lazy rescaling, as in the training kernel; only
 //     ragged tile ends mask.
-//   * The 4 waves' partial (max, sum, O) are merged in LDS, in a fixed order.  When
+//   * The 4 pairs' partial (max, sum, O) are merged in LDS, in a fixed order.  When
 //     there are too few (batch, kv head) items to fill the GPU, the key axis is also
 //     split over workgroups; each split writes its partial to the workspace and a
 //     small combine kernel merges them (same fixed order, so results are
@@ -37,18 +41,24 @@ namespace {
 
 constexpr int kTN = 32;     // keys per tile
 constexpr int kNQB = 2;     // column blocks (32 query rows each) per workgroup
-constexpr int kWaves = 4;
+constexpr int kPairs = 4;   // key lanes: lane pair p streams tiles p, p + 4, ... of its split
+constexpr int kWaves = kPairs * kNQB;  // wave = 2 * pair + column block
+constexpr int kThreads = kWaves * 64;
+constexpr float kBound = 65536.f;      // lane sum of a block's numerators forcing a rescale
+constexpr float kNegBig = -1e30f;      // "no key yet" running max
 
 template <int D>
-__global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
+__global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p) {
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TILE = kTN * D;            // elements of one K or V tile
-  constexpr int NI = kTN * (D / 8) / 64;   // load instructions per K (or V) tile
+  constexpr int RING = 2 * 2 * TILE * 2;   // bytes of a pair's ring: 2 stages x (K, V)
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
+  const int pair = wave >> 1;
+  const int qi = wave & 1;  // this wave's column block within the workgroup
 
   // ---- work item
   int w = blockIdx.x;
@@ -60,54 +70,48 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
   const int hk = bhk % p.Hkv;
   const int S = p.S, C = p.C;
 
-  // column blocks served by this workgroup
-  int cb_valid[kNQB], cb_hq[kNQB], cb_r0[kNQB];
-#pragma unroll
-  for (int i = 0; i < kNQB; ++i) {
-    const int cbg = qg * kNQB + i;
-    cb_valid[i] = cbg < p.ncb;
-    const int hh = cb_valid[i] ? cbg / p.nrc : 0;
-    cb_hq[i] = hk * p.g + hh;
-    cb_r0[i] = cb_valid[i] ? (cbg % p.nrc) * 32 : 0;
-  }
+  // this wave's column block: 32 query rows of one query head of the kv head's group
+  const int cbg = qg * kNQB + qi;
+  const bool cb_valid = cbg < p.ncb;
+  const int cb_hq = hk * p.g + (cb_valid ? cbg / p.nrc : 0);
+  const int cb_r0 = cb_valid ? (cbg % p.nrc) * 32 : 0;
 
-  // ---- key tiles of this split
+  // ---- key tiles of this split; pair p takes tiles t_begin + p + 4 r
   const int t_begin = (int)((long long)p.n_tiles * split / p.n_split);
   const int t_end = (int)((long long)p.n_tiles * (split + 1) / p.n_split);
+  const int rounds = (t_end - t_begin + kPairs - 1) / kPairs;
 
   const size_t kv_bh = (size_t)b * p.Hkv + hk;
   const __amdgpu_buffer_rsrc_t rkc = make_rsrc(p.k_cache + kv_bh * (size_t)p.cap * D, (uint32_t)C * D * 2u);
   const __amdgpu_buffer_rsrc_t rvc = make_rsrc(p.v_cache + kv_bh * (size_t)p.cap * D, (uint32_t)C * D * 2u);
   const __amdgpu_buffer_rsrc_t rkb = make_rsrc(p.k_blk + kv_bh * (size_t)S * D, (uint32_t)S * D * 2u);
   const __amdgpu_buffer_rsrc_t rvb = make_rsrc(p.v_blk + kv_bh * (size_t)S * D, (uint32_t)S * D * 2u);
-  TileLoader<D, kTN, 1> loader;  // each wave loads its own tiles
-  loader.init(0, lane);
+  TileLoader<D, kTN, 2> loader;  // the two waves of a pair load half of each tile
+  loader.init(qi, lane);
 
-  char E2D2_LDS* my = (char E2D2_LDS*)smem_raw + wave * (2 * 2 * TILE * 2);  // [stage][K, V]
+  char E2D2_LDS* ring = (char E2D2_LDS*)smem_raw + pair * RING;
   auto issue = [&](int t, int stage) {
-    char E2D2_LDS* kt = my + stage * 2 * TILE * 2;
+    char E2D2_LDS* kt = ring + stage * 2 * TILE * 2;
     if (t < p.n_tiles_cache) {
-      loader.load(rkc, t * kTN, kt, 0);
-      loader.load(rvc, t * kTN, kt + TILE * 2, 0);
+      loader.load(rkc, t * kTN, kt, qi);
+      loader.load(rvc, t * kTN, kt + TILE * 2, qi);
     } else {
-      loader.load(rkb, (t - p.n_tiles_cache) * kTN, kt, 0);
-      loader.load(rvb, (t - p.n_tiles_cache) * kTN, kt + TILE * 2, 0);
+      loader.load(rkb, (t - p.n_tiles_cache) * kTN, kt, qi);
+      loader.load(rvb, (t - p.n_tiles_cache) * kTN, kt + TILE * 2, qi);
     }
   };
   uint32_t offA[NDB], offB[NDB];
   vt_offsets<D>(lane, offA, offB);
   uint32_t koff[NC];
   k_offsets<D>(lane, koff);
-  const uint32_t my0 = lds_addr(my);
+  const uint32_t ring0 = lds_addr(ring);
 
-  // ---- queries
-  bf16x8 qf[kNQB][NC];
-#pragma unroll
-  for (int i = 0; i < kNQB; ++i) {
-    const int r = cb_r0[i] + (lane & 31);
-    const bool ok = cb_valid[i] && r < S;
-    const __bf16* qrow =
-        p.q + (((size_t)b * p.Hq + cb_hq[i]) * S + (ok ? r : 0)) * D + ((lane >> 5) << 3);
+  // ---- queries of this wave's column block
+  bf16x8 qf[NC];
+  {
+    const int r = cb_r0 + (lane & 31);
+    const bool ok = cb_valid && r < S;
+    const __bf16* qrow = p.q + (((size_t)b * p.Hq + cb_hq) * S + (ok ? r : 0)) * D + ((lane >> 5) << 3);
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       bf16x8 v = *(const bf16x8*)(qrow + cc * 16);
@@ -115,157 +119,133 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (__bf16)0.f;
       }
-      qf[i][cc] = v;
+      qf[cc] = v;
     }
   }
 
-  f32x16 o[kNQB][NDB];
-  float m[kNQB], l[kNQB];  // m: running max in use, base-2 units; l: lane-partial sum
+  f32x16 o[NDB];
 #pragma unroll
-  for (int i = 0; i < kNQB; ++i) {
-    m[i] = -1e30f;
-    l[i] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[i][db] = zero16();
-  }
+  for (int db = 0; db < NDB; ++db) o[db] = zero16();
+  float m = kNegBig;  // running max in use, base-2 units
+  float l = 0.f;      // lane-partial sum of the bf16 numerators
   const float c = p.c;
-  const int nq = cb_valid[1] ? 2 : 1;
 
-  // ---- stream this wave's tiles: t_begin + wave, + 4, ...
-  const int first = t_begin + wave;
-  const int n_my = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
-  if (n_my > 0) issue(first, 0);
-  for (int i = 0; i < n_my; ++i) {
-    const int t = first + i * kWaves;
-    if (i + 1 < n_my) {
-      issue(t + kWaves, (i + 1) & 1);
-      wait_vmem<2 * NI>();
-    } else {
-      wait_vmem<0>();
-    }
+  // One tile from ring stage STG (a constant: the LDS reads carry it in their offset).
+  auto tile = [&](int t, auto stg) {
+    constexpr int KOFF = decltype(stg)::value * 2 * TILE * 2;
+    constexpr int VOFF = KOFF + TILE * 2;
     const bool cache = t < p.n_tiles_cache;
     const int k0 = (cache ? t : t - p.n_tiles_cache) * kTN;
     const int n = cache ? C : S;
-    const bool ragged = k0 + kTN > n;
-
-    // K operands once per tile, then S^T of every column block back to back.
-    const uint32_t kb_addr = my0 + (uint32_t)((i & 1) * 2 * TILE * 2);
-    bf16x8 kf[NC];
-    kread_block<D, 0>(kb_addr, koff, kf);
-    f32x16 sc[kNQB];
+    f32x16 sc[1];
+    qk_blocks<D, 1, KOFF>(ring0, koff, qf, sc, 1);
+    if (k0 + kTN > n) {  // ragged end of the cache or of the block
+      const int kr = k0 + ((lane >> 5) << 2);
 #pragma unroll
-    for (int qi = 0; qi < kNQB; ++qi) {
-      if (qi >= nq) break;
-      f32x16 acc = zero16();
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) acc = mfma32(kf[cc], qf[qi][cc], acc);
-      sc[qi] = acc;
+      for (int j = 0; j < 16; ++j)
+        if (kr + ((j >> 2) << 3) + (j & 3) >= n) sc[0][j] = -INFINITY;
     }
-    bf16x8 vf[2][NDB];
-    read_vt_tile32<D>(kb_addr + (uint32_t)(TILE * 2), offA, offB, vf);
-
-#pragma unroll
-    for (int qi = 0; qi < kNQB; ++qi) {
-      if (qi >= nq) break;
-      if (ragged) {
-        const int kr = k0 + ((lane >> 5) << 2);
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (kr + ((j >> 2) << 3) + (j & 3) >= n) sc[qi][j] = -INFINITY;
-      }
+    bf16x8 pb[2];
+    float rs = exp_pack(sc[0], c, -m, pb, 0.f);
+    if (__builtin_amdgcn_ballot_w64(rs > kBound) != 0) {
+      // rare: a row's numerators outgrew the bound (its first keys, or a new max)
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[qi][j]);
-      // lazy, per-row rescale: keep the running max unless the row max grew by > 2^8
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[0][j]);
       const float rmax = pair_max(mx);
-      const bool need = rmax * c > m[qi] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        if (need) {
-          const float m_new = rmax * c;
-          const float alpha = fast_exp2(m[qi] - m_new);
-          l[qi] *= alpha;
+      const bool need = pair_max(rs > kBound ? 1.f : 0.f) > 0.f;
+      if (need) {
+        const float m_new = rmax * c;
+        const float alpha = fast_exp2(m - m_new);
+        l *= alpha;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[qi][db][j] *= alpha;
-          m[qi] = m_new;
-        }
+          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        m = m_new;
       }
-      float rs = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(fmaf(sc[qi][j], c, -m[qi]));
-        sc[qi][j] = e;
-        rs += e;
-      }
-      l[qi] += rs;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 pb = to_bf16x8(sc[qi][h * 8], sc[qi][h * 8 + 1], sc[qi][h * 8 + 2],
-                                    sc[qi][h * 8 + 3], sc[qi][h * 8 + 4], sc[qi][h * 8 + 5],
-                                    sc[qi][h * 8 + 6], sc[qi][h * 8 + 7]);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[qi][db] = mfma32(vf[h][db], pb, o[qi][db]);
-      }
+      rs = exp_pack(sc[0], c, -m, pb, 0.f);
     }
-  }
+    l += rs;
+    pv_block<D, VOFF>(ring0, offA, offB, pb, o);
+  };
 
-  // ---- merge the 4 waves' partials in LDS (fixed order)
-  __syncthreads();  // every wave is done with its stream buffers
-  float* mw = (float*)smem_raw;                  // [wave][cb][32]   max (base-2 units)
-  float* lw = mw + kWaves * kNQB * 32;           // [wave][cb][64]   lane-partial sums
-  float* ow = lw + kWaves * kNQB * 64;           // [wave][cb*32 + row][D]
+  // ---- rounds: all pairs step together; one barrier per round makes the pair's
+  //      tile (loaded half by each wave) visible and frees the other stage
+  const int first = t_begin + pair;
+  if (first < t_end) issue(first, 0);
+  auto round = [&](int r, auto stg) {
+    constexpr int STG = decltype(stg)::value;
+    const int t = first + r * kPairs;
+    wait_vmem<0>();  // this wave's part of round r landed (nothing else is in flight)
+    __syncthreads();
+    if (t + kPairs < t_end) issue(t + kPairs, 1 - STG);
+    if (t < t_end && cb_valid) tile(t, IntC<STG>{});
+  };
+  for (int r = 0; r < rounds; r += 2) {
+    round(r, IntC<0>{});
+    if (r + 1 < rounds) round(r + 1, IntC<1>{});
+  }
+  const bool had = first < t_end;
+
+  // ---- merge the 4 pairs' partials per column block in LDS (fixed order)
+  __syncthreads();  // every wave is done with the rings
+  float* mw = (float*)smem_raw;             // [pair][cb][32]   max (base-2 units)
+  float* lw = mw + kPairs * kNQB * 32;      // [pair][cb][64]   lane-partial sums
+  float* ow = lw + kPairs * kNQB * 64;      // [pair][cb*32 + row][D]
   const int row = lane & 31;
-#pragma unroll
-  for (int qi = 0; qi < kNQB; ++qi) {
-    const float ms = n_my > 0 ? m[qi] : -INFINITY;
-    if (lane < 32) mw[(wave * kNQB + qi) * 32 + row] = ms;
-    lw[(wave * kNQB + qi) * 64 + lane] = n_my > 0 ? l[qi] : 0.f;
+  {
+    const float ms = had ? m : -INFINITY;
+    if (lane < 32) mw[(pair * kNQB + qi) * 32 + row] = ms;
+    lw[(pair * kNQB + qi) * 64 + lane] = had ? l : 0.f;
   }
   __syncthreads();
-#pragma unroll
-  for (int qi = 0; qi < kNQB; ++qi) {
+  {
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mw[(v * kNQB + qi) * 32 + row]);
-    const float mine = mw[(wave * kNQB + qi) * 32 + row];
+    for (int v = 0; v < kPairs; ++v) M = fmaxf(M, mw[(v * kNQB + qi) * 32 + row]);
+    const float mine = mw[(pair * kNQB + qi) * 32 + row];
     const float f = mine == -INFINITY ? 0.f : fast_exp2(mine - M);
-    float* dst = ow + ((size_t)wave * kNQB * 32 + qi * 32 + row) * D;
+    float* dst = ow + ((size_t)pair * kNQB * 32 + qi * 32 + row) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const int d = db * 32 + jg * 8 + ((lane >> 5) << 2);
         f32x4 v;
-        v[0] = o[qi][db][jg * 4 + 0] * f;
-        v[1] = o[qi][db][jg * 4 + 1] * f;
-        v[2] = o[qi][db][jg * 4 + 2] * f;
-        v[3] = o[qi][db][jg * 4 + 3] * f;
+        v[0] = o[db][jg * 4 + 0] * f;
+        v[1] = o[db][jg * 4 + 1] * f;
+        v[2] = o[db][jg * 4 + 2] * f;
+        v[3] = o[db][jg * 4 + 3] * f;
         *(f32x4*)(dst + d) = v;
       }
   }
   __syncthreads();
 
   // every thread: rows r = 0..63 of the workgroup, head dims in steps of 4
+  const int nq = (qg * kNQB + 1 < p.ncb) ? 2 : 1;
   if (p.visits != nullptr && threadIdx.x == 0)
     atomicAdd(p.visits, (unsigned long long)(t_end - t_begin) * nq);
   const size_t unit = ((size_t)b * p.Hkv + hk) * p.n_qgroups + qg;
-  for (int e = threadIdx.x; e < kNQB * 32 * (D / 4); e += 256) {
+  for (int e = threadIdx.x; e < kNQB * 32 * (D / 4); e += kThreads) {
     const int r = e / (D / 4);
     const int d = (e % (D / 4)) * 4;
-    const int qi = r >> 5, rr = r & 31;
-    const int grow = cb_r0[qi] + rr;
-    if (!cb_valid[qi] || grow >= S) continue;
+    const int cq = r >> 5, rr = r & 31;
+    const int cg = qg * kNQB + cq;
+    if (cg >= p.ncb) continue;
+    const int grow = (cg % p.nrc) * 32 + rr;
+    if (grow >= S) continue;
+    const int hq = hk * p.g + cg / p.nrc;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mw[(v * kNQB + qi) * 32 + rr]);
+    for (int v = 0; v < kPairs; ++v) M = fmaxf(M, mw[(v * kNQB + cq) * 32 + rr]);
     float lt = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float mv = mw[(v * kNQB + qi) * 32 + rr];
+    for (int v = 0; v < kPairs; ++v) {
+      const float mv = mw[(v * kNQB + cq) * 32 + rr];
       const float f = mv == -INFINITY ? 0.f : fast_exp2(mv - M);
-      lt += (lw[(v * kNQB + qi) * 64 + rr] + lw[(v * kNQB + qi) * 64 + rr + 32]) * f;
+      lt += (lw[(v * kNQB + cq) * 64 + rr] + lw[(v * kNQB + cq) * 64 + rr + 32]) * f;
       const f32x4 x = *(const f32x4*)(ow + ((size_t)v * kNQB * 32 + r) * D + d);
       acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
     }
@@ -276,7 +256,7 @@ __global__ __launch_bounds__(256) void denoise_bf16_kernel(DenoiseParams p) {
       ov[1] = (__bf16)(acc[1] * inv);
       ov[2] = (__bf16)(acc[2] * inv);
       ov[3] = (__bf16)(acc[3] * inv);
-      const size_t orow = ((size_t)b * p.Hq + cb_hq[qi]) * S + grow;
+      const size_t orow = ((size_t)b * p.Hq + hq) * S + grow;
       *(bf16x4*)(p.o + orow * D + d) = ov;
       if (d == 0 && p.lse != nullptr) p.lse[orow] = (M + __log2f(lt)) * 0.6931471805599453f;
     } else {
@@ -334,9 +314,9 @@ __global__ __launch_bounds__(256) void denoise_combine_kernel(DenoiseParams p) {
 
 template <int D>
 size_t denoise_smem() {
-  const size_t stream = (size_t)kWaves * 2 * 2 * kTN * D * sizeof(__bf16);
-  const size_t merge = (size_t)kWaves * kNQB * (32 + 64) * sizeof(float) +
-                       (size_t)kWaves * kNQB * 32 * D * sizeof(float);
+  const size_t stream = (size_t)kPairs * 2 * 2 * kTN * D * sizeof(__bf16);
+  const size_t merge = (size_t)kPairs * kNQB * (32 + 64) * sizeof(float) +
+                       (size_t)kPairs * kNQB * 32 * D * sizeof(float);
   return stream > merge ? stream : merge;
 }
 
@@ -349,7 +329,7 @@ hipError_t launch_denoise_d(const DenoiseParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long long units = (long long)p.B * p.Hkv * p.n_qgroups;
-  hipLaunchKernelGGL(denoise_bf16_kernel<D>, dim3((unsigned)(units * p.n_split)), dim3(256),
+  hipLaunchKernelGGL(denoise_bf16_kernel<D>, dim3((unsigned)(units * p.n_split)), dim3(kThreads),
                      smem, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
@@ -383,9 +363,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(int row_bytes, int S, in
 int denoise_splits(int B, int Hkv, int n_qgroups, int n_tiles) {
   const long long units = (long long)B * Hkv * n_qgroups;
   const long long target = 256;  // one workgroup per compute unit
-  if (units >= target || n_tiles <= 2 * kWaves) return 1;
+  if (units >= target || n_tiles <= 2 * kPairs) return 1;
   long long s = (target + units - 1) / units;
-  const long long max_s = n_tiles / (2 * kWaves);  // keep >= 2 tiles per wave
+  const long long max_s = n_tiles / (2 * kPairs);  // keep >= 2 tiles per key lane
   if (s > max_s) s = max_s;
   return s < 1 ? 1 : (int)s;
 }

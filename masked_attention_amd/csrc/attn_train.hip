@@ -278,6 +278,31 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     }
     l += rs;
   };
+  // Numerators of one 32-key block, as softmax() does for a tile (d <= 64 loop: each
+  // block's P^T is accumulated right after its numerators, so only one block's P is
+  // live); a block whose lane sum exceeds kBound rescales its rows first.
+  auto block_softmax = [&](const f32x16& sblk, bf16x8 (&pbk)[2]) {
+    float rs = exp_pack(sblk, c, -ms, pbk, 0.f);
+    if (__builtin_amdgcn_ballot_w64(rs > kBound) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sblk[j]);
+      const float rmax = pair_max(mx);
+      const bool need = pair_max(rs > kBound ? 1.f : 0.f) > 0.f;
+      if (need) {
+        const float m_new = rmax * c;
+        const float alpha = fast_exp2(ms - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        ms = m_new;
+      }
+      rs = exp_pack(sblk, c, -ms, pbk, 0.f);
+    }
+    l += rs;
+  };
   // O^T += V^T P^T for the allowed blocks of the tile in stage `stage`.
   auto pv = [&](int stage, const int (&cls)[2], const bf16x8 (&pb)[2][2]) {
     const uint32_t vb = lds0 + 2u * (uint32_t)(stage * STAGE + TILE);
@@ -324,10 +349,16 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       f32x16 sc[2];
       qk_blocks<D, 2, KOFF>(lds0, koff, qf, sc, want);
       if (t >= nf) mask(t, cls, sc);
-      bf16x8 pb[2][2];
-      softmax(cls, sc, pb);
-      if (cls[0]) pv_block<D, VOFF>(lds0, offA, offB, pb[0], o);
-      if (cls[1]) pv_block<D, VOFF + 64 * D>(lds0, offA, offB, pb[1], o);
+      if (cls[0]) {
+        bf16x8 pb[2];
+        block_softmax(sc[0], pb);
+        pv_block<D, VOFF>(lds0, offA, offB, pb, o);
+      }
+      if (cls[1]) {
+        bf16x8 pb[2];
+        block_softmax(sc[1], pb);
+        pv_block<D, VOFF + 64 * D>(lds0, offA, offB, pb, o);
+      }
     };
     for (int t = 0; t < ntot; t += kStages) {
       tile(t, IntC<0>{});
