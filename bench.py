@@ -270,6 +270,54 @@ def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
     )
 
 
+def bench_near_ar(steps, seed):
+    """Near-autoregressive decoding: B64 H32 (MHA) d128, a 32768-row cache, block 4.
+    Each step streams the whole cache (34 GB), so it is timed eagerly, step by step."""
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+    B, H, d, C, S = 64, 32, 128, 32768, 4
+    cap = C + 16 * S
+    kc = torch.empty((B, H, cap, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    device_fill(kc, seed, tensor_id(K.K_CACHE), rows=C)
+    device_fill(vc, seed, tensor_id(K.V_CACHE), rows=C)
+
+    def fill(kind, t):
+        x = torch.empty((B, H, S, d), dtype=torch.bfloat16, device=dev)
+        device_fill(x, seed, tensor_id(kind, step=t))
+        return x
+
+    qs = [fill(K.Q_BLK, t) for t in range(steps)]
+    ks = [fill(K.K_BLK, t) for t in range(steps)]
+    vs = [fill(K.V_BLK, t) for t in range(steps)]
+    kn, vn = fill(K.K_NEW, 0), fill(K.V_NEW, 0)
+    o = torch.empty((B, H, S, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, S), device=dev)
+    assert m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, H, H, S, d, C) == 0
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        m.e2d2_attn_denoise_step(qs[t], kc, vc, C, ks[t], vs[t], o, lse_blk=lse)
+
+    for t in range(steps):  # warm-up (each step is several ms of sustained streaming)
+        step(t)
+    ms = []
+    for t in range(steps):
+        _, one = timed_launches(lambda: step(t), 1, stream)
+        ms.append(one)
+    _, app = timed_launches(lambda: m.e2d2_kv_cache_append(kc, vc, C, kn, vn), 1, stream)
+    alg = 2 * B * H * C * d * 2 + 2 * B * H * S * d * 2 + B * H * S * d * 2 + B * H * S * d * 2 + B * H * S * 4
+    med = sorted(ms)[len(ms) // 2]
+    return dict(workload="near-AR denoise step, B64 H32 (MHA) d128 cache 32768 block 4, bf16",
+                ms_per_step=med, steps_timed=len(ms), algorithmic_bytes_per_step=alg,
+                gbs=alg / (med * 1e-3) / 1e9, frac_of_hbm_peak=alg / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                append_us=app * 1e3)
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """fp64 oracle on a bounded sample of the training workload (whole heads, encoder
     and decoder), in useful TFLOP/s like the GPU figure."""
@@ -309,7 +357,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["all", "train", "denoise", "long", "copycal"],
+    ap.add_argument("--only", choices=["all", "train", "denoise", "long", "nearar", "copycal"],
                     default="all",
                     help="restrict the run (profiling); 'copycal' runs only a plain 1 GiB "
                          "device copy, the reference for scaling HBM byte counters")
@@ -357,6 +405,11 @@ def main():
         print(f"[bench] denoise: warm {out['denoise']['us_per_step_warm']:.1f} us "
               f"({out['denoise']['gbs_warm']:.0f} GB/s), cold {out['denoise']['us_per_step_cold']:.1f} us "
               f"({out['denoise']['gbs_cold']:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    if args.only in ("all", "nearar"):
+        out["near_ar"] = bench_near_ar(8, 0xE2D20005)
+        print(f"[bench] near-AR: {out['near_ar']['ms_per_step']:.3f} ms/step "
+              f"({out['near_ar']['gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
 
     if train is None:
         print(json.dumps(out))
