@@ -8,24 +8,24 @@
 //           decoder's 2L-key mask; the FLOPs table whose halved attention term is what
 //           skipping masked tiles realises).
 //
-// bf16 kernel, one workgroup = 4 waves = 128 query rows of one (batch, query head):
+// bf16 kernel, one workgroup = 4 waves = 128 query rows of one (batch, query head, kind):
 //   * Each wave owns 32 query rows and keeps their Q fragments in registers.
 //   * The key axis is walked one 64-key tile at a time, source by source (clean
 //     context keys, then, for the decoder, the noised keys of the own blocks), over
 //     exactly the tiles that hold an allowed pair (schedule.h).  K and V tiles go from
-//     HBM straight into a 4-deep ring of swizzled LDS stages (buffer_load ... lds);
-//     tile t+3 is in flight while tile t is computed.
+//     HBM straight into a 2-deep ring of swizzled LDS stages (buffer_load ... lds);
+//     tile t+1 is in flight while tile t is computed, and other workgroups on the CU
+//     (4 at d <= 64, 2 at d = 128) fill the gaps.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so a
-//     lane holds 16 keys of ONE query row: the row max is an in-lane reduction plus one
-//     exchange with lane l^32, and the row sum needs no exchange until the end.
-//   * The loop is software-pipelined: the MFMAs of S^T for tile t+1 are issued next to
-//     the softmax of tile t, then O^T += V^T P^T for tile t (V^T from the transposing
-//     LDS read).
+//     lane holds 16 keys of ONE query row: row reductions are in-lane plus, when
+//     needed, one exchange with lane l^32.
 //   * Online softmax in base 2 with the scale folded in (p = 2^(s*c - m), c =
-//     scale*log2 e) and lazy rescaling: a row keeps its running max m until its scores
-//     exceed it by more than 2^8, so O and l are rescaled only on those rare tiles (the
-//     result is the same softmax; p <= 2^8 stays well inside bf16 and fp32 range).
-//     The decision is per row, so a row's arithmetic depends on its own keys only.
+//     scale*log2 e), p packed to bf16 and summed with v_dot2 (the denominator adds the
+//     same rounded values the PV MFMA multiplies).  Rescaling is lazy: a row keeps its
+//     running max until a lane's block sum of p exceeds 2^16, then takes the block's
+//     max (the same softmax; p stays far inside bf16 and fp32 range).  The decision is
+//     per row, so a row's arithmetic depends on its own keys only.
+//   * O^T += V^T P^T per 32-key block, V^T from the transposing LDS read.
 //   * Within a tile, each wave classifies its 32x32 key blocks: empty blocks are
 //     skipped (no MFMA), full blocks skip the mask, the rest mask per element.
 //   * Epilogue: O = O^T / l in bf16, LSE = (m + log2 l) ln 2 in fp32.
@@ -44,24 +44,23 @@ constexpr int kBN = 64;           // keys per tile
 constexpr float kBound = 65536.f; // lane sum of a tile's numerators that forces a rescale
 constexpr float kNegBig = -1e30f; // "no key yet" running max (finite: no inf - inf)
 
-// Loop structure per head dimension (measured on MI355X).  LDS bounds the design:
-// workgroups per CU x ring depth x tile bytes must fit in 160 KiB.
-//   d <= 64: a tile-at-a-time loop light enough for 4 waves per SIMD; 128 query rows
-//     (4 waves) per workgroup and a 2-deep ring (32 KiB at d = 64), so four workgroups
-//     share a CU and one wave's softmax overlaps another's MFMAs.  (Measured faster than
-//     256-row workgroups with a 4-deep ring at two per CU: 55.5 vs 64.8 us on the
-//     B8 H16 L1024 S16 training forward.)
-//   d = 128: the accumulators allow one wave per SIMD, so the loop is software-
-//     pipelined instead (S^T of tile t+1 beside the softmax of tile t), 128 rows, 4-deep
-//     ring.
+// Workgroup shape per head dimension (measured on MI355X).  128 query rows (4 waves of
+// 32) per workgroup and a 2-deep ring of 64-key K/V tiles; LDS and registers decide how
+// many workgroups share a CU:
+//   d <= 64: <= 128 VGPRs and 32 KiB of LDS (d = 64), four workgroups per CU, so one
+//     wave's softmax overlaps another's MFMAs.  (Measured: 256-row workgroups with a
+//     4-deep ring at two per CU, and 3-deep rings at three per CU, are slower.)
+//   d = 128: <= 256 VGPRs and 64 KiB of LDS, two workgroups per CU.  (Measured 1.07 vs
+//     1.55 ms on the B2 Hq16/8 L8192 S64 forward against one workgroup per CU with a
+//     4-deep ring and S^T of tile t+1 software-pipelined beside the softmax of tile t,
+//     and 1.11 ms for 256-row workgroups at one per CU.)
 template <int D>
 struct LoopCfg {
-  static constexpr bool kPipelined = D > 64;
   static constexpr int kBM = 128;
   static constexpr int kWaves = kBM / 32;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kStages = D > 64 ? 4 : 2;
-  static constexpr int kBlocksPerCU = D > 64 ? 1 : 4;
+  static constexpr int kStages = 2;
+  static constexpr int kBlocksPerCU = D > 64 ? 2 : 4;
 };
 
 template <int D>
@@ -142,12 +141,10 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     }
   };
 
-  if constexpr (!LoopCfg<D>::kPipelined) {
-    // first tiles in flight before the per-row setup below
+  // first tiles in flight before the per-row setup below
 #pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
-      if (i < ntot) issue(i);
-  }
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < ntot) issue(i);
 
   // ---- per-wave rows and per-lane query row
   const int wq0 = q0 + wave * 32;
@@ -219,11 +216,6 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   float l = 0.f;       // lane-partial running sum, relative to ms
   const float c = p.c;
 
-  // S^T of tile t for this wave (blocks with cls == 0 are left untouched).
-  auto qk = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
-    const int want = (cls[0] ? 1 : 0) | (cls[1] ? 2 : 0);
-    if (want) qk_blocks<D, 2>(lds0 + 2u * (uint32_t)((t % kStages) * STAGE), koff, qf, sc, want);
-  };
   // Element mask of the partly allowed blocks of tile t.
   auto mask = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
     const int src = tsrc(t);
@@ -240,47 +232,13 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       }
     }
   };
-  // Numerators of tile t against the running max (online softmax, base 2), packed to
-  // bf16; returns the lane's sum of them.  Rescaling is lazy and needs no row max on
-  // the common path: when a lane's sum exceeds kBound (the row's first keys, or scores
-  // that outgrew the running max), the row takes its max over the tile, rescales O and
-  // l, and the tile's numerators are formed again.  The decision is per row (the lane
-  // pair), so a row's arithmetic depends on its own keys only.
-  auto softmax = [&](const int (&cls)[2], const f32x16 (&sc)[2], bf16x8 (&pb)[2][2]) {
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (cls[kb]) rs = exp_pack(sc[kb], c, -ms, pb[kb], rs);
-    if (__builtin_amdgcn_ballot_w64(rs > kBound) != 0) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (cls[kb]) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
-        }
-      const float rmax = pair_max(mx);
-      const bool need = pair_max(rs > kBound ? 1.f : 0.f) > 0.f;
-      if (need) {
-        const float m_new = rmax * c;
-        const float alpha = fast_exp2(ms - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-        ms = m_new;
-      }
-      rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (cls[kb]) rs = exp_pack(sc[kb], c, -ms, pb[kb], rs);
-    }
-    l += rs;
-  };
-  // Numerators of one 32-key block, as softmax() does for a tile (d <= 64 loop: each
-  // block's P^T is accumulated right after its numerators, so only one block's P is
-  // live); a block whose lane sum exceeds kBound rescales its rows first.
+  // Numerators of one 32-key block against the running max (online softmax, base 2),
+  // packed to bf16, their lane sum added to l.  Rescaling is lazy and needs no row max
+  // on the common path: when a lane's sum exceeds kBound (the row's first keys, or
+  // scores that outgrew the running max), the row takes its max over the block,
+  // rescales O and l, and the block's numerators are formed again.  The decision is
+  // per row (the lane pair), so a row's arithmetic depends on its own keys only.  Each
+  // block's P^T is accumulated right after its numerators, so one block's P is live.
   auto block_softmax = [&](const f32x16& sblk, bf16x8 (&pbk)[2]) {
     float rs = exp_pack(sblk, c, -ms, pbk, 0.f);
     if (__builtin_amdgcn_ballot_w64(rs > kBound) != 0) {
@@ -303,15 +261,7 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     }
     l += rs;
   };
-  // O^T += V^T P^T for the allowed blocks of the tile in stage `stage`.
-  auto pv = [&](int stage, const int (&cls)[2], const bf16x8 (&pb)[2][2]) {
-    const uint32_t vb = lds0 + 2u * (uint32_t)(stage * STAGE + TILE);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (cls[kb]) pv_block<D, 0>(vb + (uint32_t)(kb * 64 * D), offA, offB, pb[kb], o);
-  };
-
-  if constexpr (!LoopCfg<D>::kPipelined) {
+  {
     // ---- one tile at a time through a kStages-deep ring: tiles t+1 .. t+kStages-1 are
     //      in flight while tile t is computed.  Unrolled by kStages so the stage of each
     //      tile is a constant that the LDS reads carry in their offset field.  Tiles
@@ -369,91 +319,6 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       if constexpr (kStages > 3) {
         if (t + 3 < ntot) tile(t + 3, IntC<3 % kStages>{});
       }
-    }
-  } else {
-  // ---- prologue: tiles 0 .. kStages-2 in flight, tile 0 landed, S^T of tile 0
-    f32x16 sA[2], sB[2];
-    int cA[2] = {0, 0}, cB[2] = {0, 0};
-    if (ntot > 0) {
-  #pragma unroll
-      for (int i = 0; i < kStages - 1; ++i)
-        if (i < ntot) issue(i);
-      static_assert(kStages >= 3 && kStages <= 4, "S^T of tile t+1 is formed during step t");
-      const int after0 = min(kStages - 2, ntot - 1);  // tiles issued after tile 0
-      if (after0 >= 2) wait_vmem<2 * NIW>();
-      else if (after0 == 1) wait_vmem<NIW>();
-      else wait_vmem<0>();
-      __syncthreads();
-      classify_tile(0, cA);
-      qk(0, cA, sA);
-    }
-
-    // ---- main loop.  Tiles [0, nf) are full for every row of the workgroup (they hold
-    //      keys of blocks strictly before the first row's block), so they take a
-    //      branch-free path with no classification and no mask.  The loop is unrolled
-    //      by two so the score buffers alternate without copies.
-    int nf = 0;
-    {
-      const Interval cm = common_interval(kind, 0, q0, r_last, S, L, 0);
-      nf = min(cm.hi / kBN, tr0.last) - tr0.first;  // whole tiles inside [0, common hi)
-      nf = max(0, min(nf, n0));
-    }
-    auto sync_and_issue = [&](int t) {
-      if (t + 1 < ntot) {
-        // tile t+1 must have landed; the tiles issued after it (t+2 .. t+kStages-2)
-        // may stay in flight
-        if (kStages >= 4 && t + 2 < ntot) wait_vmem<(kStages - 3) * NIW>();
-        else wait_vmem<0>();
-      }
-      __syncthreads();  // everyone is done with tile t-1; its stage is free
-      if (t + kStages - 1 < ntot) issue(t + kStages - 1);
-    };
-    // Full tile t (and full tile t+1): S^T(t+1) on the MFMA beside softmax(t), then PV(t).
-    auto fast_step = [&](int t, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
-      sync_and_issue(t);
-      if (!wave_live) return;
-      qk_blocks<D, 2>(lds0 + 2u * (uint32_t)(((t + 1) % kStages) * STAGE), koff, qf, snext, 3);
-      const int all[2] = {2, 2};
-      bf16x8 pb[2][2];
-      softmax(all, scur, pb);
-      pv(t % kStages, all, pb);
-    };
-    // Any tile: classification, masks and skips.
-    auto step = [&](int t, int (&cc)[2], f32x16 (&scur)[2], int (&cn)[2], f32x16 (&snext)[2]) {
-      sync_and_issue(t);
-      if (t + 1 < ntot) {
-        classify_tile(t + 1, cn);
-        qk(t + 1, cn, snext);
-      }
-      if (!cc[0] && !cc[1]) return;
-      mask(t, cc, scur);
-      bf16x8 pb[2][2];
-      softmax(cc, scur, pb);
-      pv(t % kStages, cc, pb);
-    };
-    int t = 0;
-    // fast region: steps t with t + 1 < nf (tiles t and t+1 both full)
-    for (; t + 2 < nf; t += 2) {
-      fast_step(t, sA, sB);
-      fast_step(t + 1, sB, sA);
-    }
-    if (t + 1 < nf) {
-      fast_step(t, sA, sB);
-      ++t;
-      // tile t's scores are now in sB: continue the general loop from there
-      cB[0] = cB[1] = wave_live ? 2 : 0;
-      for (; t + 1 < ntot; t += 2) {
-        step(t, cB, sB, cA, sA);
-        step(t + 1, cA, sA, cB, sB);
-      }
-      if (t < ntot) step(t, cB, sB, cA, sA);
-    } else {
-      if (t > 0) cA[0] = cA[1] = wave_live ? 2 : 0;  // tile t < nf is full
-      for (; t + 1 < ntot; t += 2) {
-        step(t, cA, sA, cB, sB);
-        step(t + 1, cB, sB, cA, sA);
-      }
-      if (t < ntot) step(t, cA, sA, cB, sB);
     }
   }
 
