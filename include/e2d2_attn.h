@@ -137,6 +137,38 @@ e2d2_status e2d2_kv_cache_append(int dtype, int B, int Hkv, int S, int d, void* 
                                  void* v_cache, long long cache_len, long long cache_cap,
                                  const void* k_new, const void* v_new, void* stream);
 
+/* One denoising step for a batch whose sequences sit at different points of the
+ * sampling loop ([Notes] §3 采样算法: each sequence's cache grows by one block per
+ * finished block, so in a batch decoded together the cached lengths differ).  Same as
+ * e2d2_attn_denoise_step, except that sequence b attends rows [0, cache_lens[b]) of
+ * its cache:
+ *   cache_lens: device array of B int32 (4-byte aligned), read by the kernel when it
+ *   runs, so a captured HIP graph of this call stays valid while the caller updates
+ *   the lengths on the device; each length is clamped to [0, max_cache_len].
+ *   max_cache_len: host bound on every length (0 <= max_cache_len <= cache_cap); it
+ *   sizes the launch and the workspace (e2d2_attn_denoise_workspace_bytes with
+ *   cache_len = max_cache_len).
+ *   bf16 only (fp32: E2D2_ERR_UNSUPPORTED).  Errors as e2d2_attn_denoise_step, plus
+ *   E2D2_ERR_NULL for a NULL cache_lens. */
+e2d2_status e2d2_attn_denoise_step_varlen(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                          float scale, const void* q_blk, const void* k_cache,
+                                          const void* v_cache, const int* cache_lens,
+                                          long long max_cache_len, long long cache_cap,
+                                          const void* k_blk, const void* v_blk, void* o_blk,
+                                          float* lse_blk, void* workspace, size_t workspace_bytes,
+                                          unsigned long long* dbg_tile_visits, void* stream);
+
+/* KV-cache append for sequences of different lengths ([Notes] §3 采样算法): sequence b's
+ * k_new, v_new rows go to rows [cache_lens[b], cache_lens[b] + S) of its cache.
+ *   cache_lens: device array of B int32 read when the kernel runs; a sequence whose
+ *   length is outside [0, max_cache_len] is left untouched (the call cannot report
+ *   it).  Needs max_cache_len + S <= cache_cap (else E2D2_ERR_CAPACITY).  The caller
+ *   then advances the lengths it appended to by S.  Bitwise copy. */
+e2d2_status e2d2_kv_cache_append_varlen(int dtype, int B, int Hkv, int S, int d, void* k_cache,
+                                        void* v_cache, const int* cache_lens,
+                                        long long max_cache_len, long long cache_cap,
+                                        const void* k_new, const void* v_new, void* stream);
+
 /* Query/key tile shape (bm query rows of one head, bn keys) the kernels use for a
  * kind, dtype and head dimension.  Host-only; bm and bn are host pointers. */
 e2d2_status e2d2_attn_tile_shape(int kind, int dtype, int d, int* bm, int* bn);

@@ -50,6 +50,10 @@ _SIGS = {
     "e2d2_attn_denoise_step": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _ll, _ll, _vp, _vp,
                                     _vp, _vp, _vp, _sz, _vp, _vp]),
     "e2d2_kv_cache_append": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _ll, _ll, _vp, _vp, _vp]),
+    "e2d2_attn_denoise_step_varlen": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _ll, _ll,
+                                           _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "e2d2_kv_cache_append_varlen": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _ll, _ll, _vp, _vp,
+                                         _vp]),
     "e2d2_attn_tile_shape": (_i, [_i, _i, _i, _int_p, _int_p]),
     "e2d2_attn_count_tiles": (_i, [_i, _i, _i, _i, _i, _ll, _i, _i, _ull_p, _ull_p]),
 }
@@ -205,6 +209,55 @@ def e2d2_attn_denoise_step(q_blk, k_cache, v_cache, cache_len: int, k_blk, v_blk
         _opt(lse_blk, "lse_blk", 3), ws_ptr, ws_bytes, _opt(tile_visits, "tile_visits", 1),
         _stream(q_blk))
     _check("e2d2_attn_denoise_step", st)
+
+
+def _lens(cache_lens, B):
+    if (cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,)
+            or not cache_lens.is_contiguous()):
+        raise ValueError("cache_lens must be a contiguous int32 tensor [B]")
+    return _dev(cache_lens, "cache_lens", 1)
+
+
+def e2d2_attn_denoise_step_varlen(q_blk, k_cache, v_cache, cache_lens, max_cache_len: int, k_blk,
+                                  v_blk, o_blk, lse_blk=None, workspace=None, scale=None,
+                                  tile_visits=None):
+    """One denoising step where sequence b attends cache rows [0, cache_lens[b]);
+    ``cache_lens`` is an int32 CUDA tensor [B] read on the device (each length clamped
+    to [0, max_cache_len]), other arguments as e2d2_attn_denoise_step."""
+    B, Hq, S, d = q_blk.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    _same(q_blk.dtype, k_cache, v_cache, k_blk, v_blk, o_blk)
+    if tuple(k_cache.shape) != (B, Hkv, cap, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, cap, d]")
+    if tuple(k_blk.shape) != (B, Hkv, S, d) or v_blk.shape != k_blk.shape or o_blk.shape != q_blk.shape:
+        raise ValueError("shape mismatch")
+    if lse_blk is not None and (lse_blk.dtype != torch.float32 or tuple(lse_blk.shape) != (B, Hq, S)):
+        raise ValueError("lse must be float32 [B, Hq, S]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace", workspace.dim()), workspace.numel() * workspace.element_size()
+    st = lib().e2d2_attn_denoise_step_varlen(
+        _dtype_code(q_blk), B, Hq, Hkv, S, d, _default_scale(d, scale), _dev(q_blk, "q_blk"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _lens(cache_lens, B),
+        int(max_cache_len), cap, _dev(k_blk, "k_blk"), _dev(v_blk, "v_blk"),
+        _dev(o_blk, "o_blk"), _opt(lse_blk, "lse_blk", 3), ws_ptr, ws_bytes,
+        _opt(tile_visits, "tile_visits", 1), _stream(q_blk))
+    _check("e2d2_attn_denoise_step_varlen", st)
+
+
+def e2d2_kv_cache_append_varlen(k_cache, v_cache, cache_lens, max_cache_len: int, k_new, v_new):
+    """Copy k_new/v_new [B, Hkv, S, d] of sequence b into its cache rows
+    [cache_lens[b], cache_lens[b] + S) (cache_lens: int32 CUDA tensor [B])."""
+    B, Hkv, cap, d = k_cache.shape
+    S = k_new.shape[2]
+    _same(k_cache.dtype, v_cache, k_new, v_new)
+    if v_cache.shape != k_cache.shape or tuple(k_new.shape) != (B, Hkv, S, d) or v_new.shape != k_new.shape:
+        raise ValueError("shape mismatch")
+    st = lib().e2d2_kv_cache_append_varlen(
+        _dtype_code(k_cache), B, Hkv, S, d, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _lens(cache_lens, B), int(max_cache_len), cap, _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _stream(k_cache))
+    _check("e2d2_kv_cache_append_varlen", st)
 
 
 def e2d2_kv_cache_append(k_cache, v_cache, cache_len: int, k_new, v_new):

@@ -213,13 +213,18 @@ size_t e2d2_attn_denoise_workspace_bytes(int dtype, int B, int Hq, int Hkv, int 
   return denoise_ws_bytes(dtype, B, Hq, Hkv, S, d, cache_len);
 }
 
-e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float scale,
-                                   const void* q_blk, const void* k_cache, const void* v_cache,
-                                   long long cache_len, long long cache_cap, const void* k_blk,
-                                   const void* v_blk, void* o_blk, float* lse_blk, void* workspace,
-                                   size_t workspace_bytes, unsigned long long* dbg_tile_visits,
-                                   void* stream) {
+namespace {
+
+// Shared by the uniform and the per-sequence denoise calls (lens == NULL: every
+// sequence has cache_len rows; else sequence b has lens[b], at most cache_len).
+e2d2_status denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float scale,
+                         const void* q_blk, const void* k_cache, const void* v_cache,
+                         const int* lens, long long cache_len, long long cache_cap,
+                         const void* k_blk, const void* v_blk, void* o_blk, float* lse_blk,
+                         void* workspace, size_t workspace_bytes,
+                         unsigned long long* dbg_tile_visits, void* stream) {
   if (dtype != E2D2_F32 && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
+  if (lens != nullptr && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
   if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Hq % Hkv != 0 || !scale_ok(scale))
     return E2D2_ERR_SHAPE;
@@ -250,6 +255,7 @@ e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int
     p.v_blk = (const __bf16*)v_blk;
     p.o = (__bf16*)o_blk;
     p.lse = lse_blk;
+    p.lens = lens;
     if (need > 0) {
       const size_t rows = (size_t)B * Hkv * sh.n_qgroups * sh.n_split * 64;
       p.ws_o = (float*)workspace;
@@ -288,6 +294,53 @@ e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int
   p.n_qtiles = cdiv(S, e2d2::kF32TileBM);
   if ((long long)B * Hq * p.n_qtiles > INT32_MAX) return E2D2_ERR_SHAPE;
   return hip_status(e2d2::launch_attn_f32(p, d, s));
+}
+
+}  // namespace
+
+e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float scale,
+                                   const void* q_blk, const void* k_cache, const void* v_cache,
+                                   long long cache_len, long long cache_cap, const void* k_blk,
+                                   const void* v_blk, void* o_blk, float* lse_blk, void* workspace,
+                                   size_t workspace_bytes, unsigned long long* dbg_tile_visits,
+                                   void* stream) {
+  return denoise_step(dtype, B, Hq, Hkv, S, d, scale, q_blk, k_cache, v_cache, nullptr, cache_len,
+                      cache_cap, k_blk, v_blk, o_blk, lse_blk, workspace, workspace_bytes,
+                      dbg_tile_visits, stream);
+}
+
+e2d2_status e2d2_attn_denoise_step_varlen(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                          float scale, const void* q_blk, const void* k_cache,
+                                          const void* v_cache, const int* cache_lens,
+                                          long long max_cache_len, long long cache_cap,
+                                          const void* k_blk, const void* v_blk, void* o_blk,
+                                          float* lse_blk, void* workspace, size_t workspace_bytes,
+                                          unsigned long long* dbg_tile_visits, void* stream) {
+  if (cache_lens == nullptr) return E2D2_ERR_NULL;
+  if (((uintptr_t)cache_lens & 3u) != 0) return E2D2_ERR_SHAPE;
+  if (max_cache_len > 0 && (!k_cache || !v_cache)) return E2D2_ERR_NULL;
+  return denoise_step(dtype, B, Hq, Hkv, S, d, scale, q_blk, k_cache, v_cache, cache_lens,
+                      max_cache_len, cache_cap, k_blk, v_blk, o_blk, lse_blk, workspace,
+                      workspace_bytes, dbg_tile_visits, stream);
+}
+
+e2d2_status e2d2_kv_cache_append_varlen(int dtype, int B, int Hkv, int S, int d, void* k_cache,
+                                        void* v_cache, const int* cache_lens,
+                                        long long max_cache_len, long long cache_cap,
+                                        const void* k_new, const void* v_new, void* stream) {
+  if (dtype != E2D2_F32 && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
+  if (B <= 0 || Hkv <= 0 || S <= 0 || max_cache_len < 0 || cache_cap <= 0 ||
+      cache_cap > kMaxLen)
+    return E2D2_ERR_SHAPE;
+  if (max_cache_len + S > cache_cap) return E2D2_ERR_CAPACITY;
+  if (!k_cache || !v_cache || !k_new || !v_new || !cache_lens) return E2D2_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+      ((uintptr_t)cache_lens & 3u) != 0)
+    return E2D2_ERR_SHAPE;
+  return hip_status(e2d2::launch_kv_append_varlen(dtype == E2D2_BF16 ? 2 : 4, B, Hkv, S, d,
+                                                  k_cache, v_cache, cache_lens, max_cache_len,
+                                                  cache_cap, k_new, v_new, (hipStream_t)stream));
 }
 
 e2d2_status e2d2_kv_cache_append(int dtype, int B, int Hkv, int S, int d, void* k_cache,

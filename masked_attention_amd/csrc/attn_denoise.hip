@@ -68,7 +68,11 @@ __global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p)
   const int bhk = w / p.n_qgroups;
   const int b = bhk / p.Hkv;
   const int hk = bhk % p.Hkv;
-  const int S = p.S, C = p.C;
+  const int S = p.S;
+  // this sequence's cache length (per-sequence lengths live on the device, so one
+  // captured launch serves every step of a decode loop)
+  const int C = p.lens != nullptr ? min(max(p.lens[b], 0), p.C) : p.C;
+  const int tiles_c = (C + kTN - 1) / kTN;  // cache tiles of this sequence (<= n_tiles_cache)
 
   // this wave's column block: 32 query rows of one query head of the kv head's group
   const int cbg = qg * kNQB + qi;
@@ -90,6 +94,8 @@ __global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p)
   loader.init(qi, lane);
 
   char E2D2_LDS* ring = (char E2D2_LDS*)smem_raw + pair * RING;
+  // tile t holds keys of this sequence: a cache tile below its length, or an own-block tile
+  auto live = [&](int t) { return t < p.n_tiles_cache ? t < tiles_c : true; };
   auto issue = [&](int t, int stage) {
     char E2D2_LDS* kt = ring + stage * 2 * TILE * 2;
     if (t < p.n_tiles_cache) {
@@ -173,20 +179,24 @@ __global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p)
   // ---- rounds: all pairs step together; one barrier per round makes the pair's
   //      tile (loaded half by each wave) visible and frees the other stage
   const int first = t_begin + pair;
-  if (first < t_end) issue(first, 0);
+  if (first < t_end && live(first)) issue(first, 0);
+  int done = 0;  // tiles this wave computed
   auto round = [&](int r, auto stg) {
     constexpr int STG = decltype(stg)::value;
     const int t = first + r * kPairs;
     wait_vmem<0>();  // this wave's part of round r landed (nothing else is in flight)
     __syncthreads();
-    if (t + kPairs < t_end) issue(t + kPairs, 1 - STG);
-    if (t < t_end && cb_valid) tile(t, IntC<STG>{});
+    if (t + kPairs < t_end && live(t + kPairs)) issue(t + kPairs, 1 - STG);
+    if (t < t_end && live(t) && cb_valid) {
+      tile(t, IntC<STG>{});
+      ++done;
+    }
   };
   for (int r = 0; r < rounds; r += 2) {
     round(r, IntC<0>{});
     if (r + 1 < rounds) round(r + 1, IntC<1>{});
   }
-  const bool had = first < t_end;
+  const bool had = done > 0;
 
   // ---- merge the 4 pairs' partials per column block in LDS (fixed order)
   __syncthreads();  // every wave is done with the rings
@@ -223,9 +233,7 @@ __global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p)
   __syncthreads();
 
   // every thread: rows r = 0..63 of the workgroup, head dims in steps of 4
-  const int nq = (qg * kNQB + 1 < p.ncb) ? 2 : 1;
-  if (p.visits != nullptr && threadIdx.x == 0)
-    atomicAdd(p.visits, (unsigned long long)(t_end - t_begin) * nq);
+  if (p.visits != nullptr && lane == 0 && done > 0) atomicAdd(p.visits, (unsigned long long)done);
   const size_t unit = ((size_t)b * p.Hkv + hk) * p.n_qgroups + qg;
   for (int e = threadIdx.x; e < kNQB * 32 * (D / 4); e += kThreads) {
     const int r = e / (D / 4);
@@ -358,6 +366,32 @@ __global__ __launch_bounds__(256) void kv_append_kernel(int row_bytes, int S, in
   }
 }
 
+// Per-sequence append: like kv_append_kernel, with sequence b's rows written at
+// lens[b] (skipped when lens[b] is outside [0, max_len]; the host checked that
+// max_len + S fits the capacity).
+__global__ __launch_bounds__(256) void kv_append_varlen_kernel(int row_bytes, int S, int Hkv, int BH,
+                                                               char* k_cache, char* v_cache,
+                                                               const int* lens, long long max_len,
+                                                               long long cap, const char* k_new,
+                                                               const char* v_new) {
+  const int per_row = row_bytes / 16;
+  const long long per_tensor = (long long)BH * S * per_row;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * per_tensor;
+       i += (long long)gridDim.x * blockDim.x) {
+    const bool is_v = i >= per_tensor;
+    const long long j = is_v ? i - per_tensor : i;
+    const int ch = (int)(j % per_row);
+    const long long rs = j / per_row;  // (bh, s)
+    const int s = (int)(rs % S);
+    const long long bh = rs / S;
+    const long long len = lens[bh / Hkv];
+    if (len < 0 || len > max_len) continue;
+    const char* src = (is_v ? v_new : k_new) + (rs * per_row + ch) * 16;
+    char* dst = (is_v ? v_cache : k_cache) + ((bh * cap + len + s) * per_row + ch) * 16;
+    *(int4*)dst = *(const int4*)src;
+  }
+}
+
 }  // namespace
 
 int denoise_splits(int B, int Hkv, int n_qgroups, int n_tiles) {
@@ -390,6 +424,20 @@ hipError_t launch_kv_append(int elem_bytes, int B, int Hkv, int S, int d, void* 
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, row_bytes, S,
                      B * Hkv, (char*)k_cache, (char*)v_cache, cache_len, cap,
+                     (const char*)k_new, (const char*)v_new);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_varlen(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
+                                   void* v_cache, const int* lens, long long max_len, long long cap,
+                                   const void* k_new, const void* v_new, hipStream_t stream) {
+  const int row_bytes = d * elem_bytes;
+  const long long total = 2ll * B * Hkv * S * (row_bytes / 16);
+  if (total == 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(kv_append_varlen_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     row_bytes, S, Hkv, B * Hkv, (char*)k_cache, (char*)v_cache, lens, max_len, cap,
                      (const char*)k_new, (const char*)v_new);
   return hipGetLastError();
 }

@@ -53,8 +53,9 @@ struct DenoiseParams {
   float* lse;
   float* ws_o;   // [units][n_split][64][d] unnormalised partial O (n_split > 1)
   float* ws_ml;  // [units][n_split][64][2] partial (max, sum) in base-2 units
+  const int* lens;  // per-sequence cache lengths [B] on the device (clamped to [0, C]), or NULL: all C
   long long cap;
-  int C, S, B, Hq, Hkv;
+  int C, S, B, Hq, Hkv;  // C: the cache length, or with lens the largest one allowed
   int g;          // query heads per kv head
   int nrc;        // 32-row chunks per head: ceil(S / 32)
   int ncb;        // column blocks per kv head: g * nrc
@@ -81,5 +82,10 @@ int denoise_splits(int B, int Hkv, int n_qgroups, int n_tiles);
 hipError_t launch_kv_append(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
                             void* v_cache, long long cache_len, long long cap,
                             const void* k_new, const void* v_new, hipStream_t stream);
+// Per-sequence variant: sequence b appends at row lens[b] (device array); a sequence
+// whose lens[b] is outside [0, max_len] is left untouched.
+hipError_t launch_kv_append_varlen(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
+                                   void* v_cache, const int* lens, long long max_len, long long cap,
+                                   const void* k_new, const void* v_new, hipStream_t stream);
 
 }  // namespace e2d2

@@ -155,3 +155,29 @@ def test_append_validation():
     assert lib.e2d2_kv_cache_append(m.BF16, 1, 1, 4, 64, None, 16, 0, 12, 16, 16, None) == ERR_NULL
     assert lib.e2d2_kv_cache_append(m.BF16, 1, 1, 4, 64, 16, 16, -1, 12, 16, 16, None) == ERR_SHAPE
     assert lib.e2d2_kv_cache_append(m.BF16, 1, 1, 4, 40, 16, 16, 0, 12, 16, 16, None) == ERR_UNSUPPORTED
+
+
+def _varlen(**kw):
+    a = dict(dtype=m.BF16, B=1, Hq=2, Hkv=1, S=4, d=128, scale=0.1, q=16, kc=16, vc=16, lens=16,
+             C=8, cap=16, kb=16, vb=16, o=16, lse=None, ws=None, ws_bytes=0, dbg=None, stream=None)
+    a.update(kw)
+    return m.lib().e2d2_attn_denoise_step_varlen(*a.values())
+
+
+def test_denoise_varlen_validation_returns_before_launch():
+    assert _varlen(lens=None) == ERR_NULL
+    assert _varlen(lens=18) == ERR_SHAPE          # misaligned int32 array
+    assert _varlen(dtype=m.F32) == ERR_UNSUPPORTED
+    assert _varlen(C=17) == ERR_SHAPE             # max length beyond the capacity
+    assert _varlen(kc=None) == ERR_NULL
+    need = m.e2d2_attn_denoise_workspace_bytes(m.BF16, 1, 2, 1, 4, 128, 4096)
+    assert _varlen(C=4096, cap=4096, ws=16, ws_bytes=need - 1) == ERR_WORKSPACE
+
+
+def test_append_varlen_validation():
+    lib = m.lib()
+    f = lib.e2d2_kv_cache_append_varlen
+    assert f(m.BF16, 1, 1, 4, 64, 16, 16, 16, 13, 16, 16, 16, None) == ERR_CAPACITY
+    assert f(m.BF16, 1, 1, 4, 64, 16, 16, None, 12, 16, 16, 16, None) == ERR_NULL
+    assert f(m.BF16, 1, 1, 4, 64, 16, 16, 18, 12, 16, 16, 16, None) == ERR_SHAPE
+    assert f(m.BF16, 1, 1, 4, 48, 16, 16, 16, 12, 16, 16, 16, None) == ERR_UNSUPPORTED
