@@ -30,3 +30,7 @@ from .attention import (  # noqa: F401
     denoise_step,
     kv_cache_append,
 )
+from .backward import (  # noqa: F401
+    masked_softmax_attention_grad,
+    train_bwd,
+)

@@ -50,6 +50,8 @@ class TensorKind(enum.IntEnum):
     K_CACHE = 12
     V_CACHE = 13
     PROBE = 14
+    DO_DEC = 15   # upstream gradient of the decoder attention output (backward pass)
+    DO_ENC = 16   # upstream gradient of the encoder attention output
 
 
 def tensor_id(kind: int, step: int = 0, block: int = 0) -> int:
