@@ -161,6 +161,51 @@ def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True):
                 useful_flop=useful, wall_s=wall)
 
 
+def bench_train_bwd(B, Hq, Hkv, L, S, d, steps, seed):
+    """Training backward (e2d2_attn_train_bwd, encoder and decoder) after one forward;
+    `steps` backward launches replayed from one HIP graph.  Useful work: the four
+    products dV, dP, dQ, dK over the allowed pairs, 8 * d flop per pair (the score
+    recomputation is not counted)."""
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+
+    def fill(kind, H):
+        t = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=dev)
+        device_fill(t, seed, tensor_id(kind))
+        return t
+
+    qd, qe, dod, doe = fill(K.Q_DEC, Hq), fill(K.Q_ENC, Hq), fill(K.DO_DEC, Hq), fill(K.DO_ENC, Hq)
+    kc, vc, kd, vd = (fill(k, Hkv) for k in (K.K_CTX, K.V_CTX, K.K_DEC, K.V_DEC))
+    od, oe = torch.empty_like(qd), torch.empty_like(qe)
+    ld = torch.empty((B, Hq, L), device=dev)
+    le = torch.empty_like(ld)
+    m.e2d2_attn_train_fwd(qd, kc, vc, kd, vd, od, S, lse_dec=ld, q_enc=qe, o_enc=oe, lse_enc=le)
+    g = [torch.empty_like(t) for t in (qd, kc, vc, kd, vd, qe)]
+    ws = torch.empty(m.e2d2_attn_train_bwd_workspace_bytes(m.BF16, B, Hq, L, True),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        m.e2d2_attn_train_bwd(qd, kc, vc, kd, vd, od, ld, dod, S, g[0], g[1], g[2], g[3], g[4], ws,
+                              q_enc=qe, o_enc=oe, lse_enc=le, do_enc=doe, dq_enc=g[5])
+
+    step()
+    torch.cuda.synchronize()
+    graph = graph_of(step, steps)
+    clock_warmup(graph.replay)
+    stream = torch.cuda.current_stream(dev)
+    total_ms, _ = timed_launches(graph.replay, 1, stream)
+    ms = total_ms / steps
+    useful = 8.0 * d * 2 * pairs_blockcausal(L, S) * B * Hq
+    tf = useful / (ms * 1e-3) / 1e12
+    return dict(workload=f"training bwd enc+dec, B{B} Hq{Hq} Hkv{Hkv} d{d} L{L} S{S}, bf16",
+                ms_per_step=round(ms, 5), tflops=round(tf, 1),
+                frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4), useful_flop=useful)
+
+
 def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
     import torch
 
@@ -357,7 +402,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["all", "train", "denoise", "long", "nearar", "copycal"],
+    ap.add_argument("--only", choices=["all", "train", "bwd", "denoise", "long", "nearar", "copycal"],
                     default="all",
                     help="restrict the run (profiling); 'copycal' runs only a plain 1 GiB "
                          "device copy, the reference for scaling HBM byte counters")
@@ -391,6 +436,13 @@ def main():
         train = bench_train(B, H, H, L, S, d, args.steps, args.warmup, 0xE2D20002)
         print(f"[bench] train fwd B{B} H{H} d{d} L{L} S{S}: {train['ms_per_step'] * 1e3:.1f} us/step, "
               f"kernel {train['kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+    if args.only in ("all", "bwd"):
+        out["train_bwd"] = bench_train_bwd(8, 16, 16, 1024, 16, 64, args.steps, 0xE2D20002)
+        out["long_train_bwd"] = bench_train_bwd(2, 16, 8, 8192, 64, 128, max(3, args.steps // 10),
+                                                0xE2D20004)
+        for k in ("train_bwd", "long_train_bwd"):
+            print(f"[bench] {k}: {out[k]['ms_per_step'] * 1e3:.1f} us, {out[k]['tflops']} TFLOP/s",
+                  file=sys.stderr, flush=True)
     if args.only in ("all", "long"):
         lt = bench_train(2, 16, 8, 8192, 64, 128, max(3, args.steps // 10), 2, 0xE2D20004)
         out["long_train"] = dict(

@@ -106,6 +106,34 @@ e2d2_status e2d2_attn_train_fwd(int dtype, int B, int Hq, int Hkv, int L, int d,
                                 float* lse_enc, unsigned long long* dbg_tile_visits,
                                 void* stream);
 
+/* Bytes of device workspace e2d2_attn_train_bwd needs (with_enc: 1 when the encoder's
+ * gradients are computed too).  0 for unsupported arguments.  Host-only. */
+size_t e2d2_attn_train_bwd_workspace_bytes(int dtype, int B, int Hq, int L, int with_enc);
+
+/* Backward of e2d2_attn_train_fwd ([Notes] §4 训练算法: a training step backpropagates
+ * the decoder's loss through the decoder attention and, through the clean context
+ * keys/values both attentions read, into the encoder).  Gradients of the same fused
+ * attention, from the forward's outputs:
+ *   inputs: q_dec, k_ctx, v_ctx, k_dec, v_dec as in the forward; o_dec and lse_dec
+ *   (required) from the forward; do_dec [B][Hq][L][d] the gradient of o_dec.  With
+ *   q_enc (then o_enc, lse_enc, do_enc and dq_enc are all required; else all NULL)
+ *   the encoder's block-causal attention over (q_enc, k_ctx, v_ctx) is included.
+ *   outputs (overwritten, not accumulated): dq_dec [B][Hq][L][d]; dk_ctx, dv_ctx
+ *   [B][Hkv][L][d] summing the encoder's and the decoder's gradients and every query
+ *   head of a grouped kv head; dk_dec, dv_dec [B][Hkv][L][d]; dq_enc.
+ *   workspace: device scratch of e2d2_attn_train_bwd_workspace_bytes(...) bytes,
+ *   contents ignored on entry; calls sharing it must be ordered on one stream.
+ * bf16 only (fp32: E2D2_ERR_UNSUPPORTED).  Deterministic (no atomics).  Errors as the
+ * forward, plus E2D2_ERR_WORKSPACE. */
+e2d2_status e2d2_attn_train_bwd(int dtype, int B, int Hq, int Hkv, int L, int d, int S,
+                                float scale, const void* q_dec, const void* k_ctx,
+                                const void* v_ctx, const void* k_dec, const void* v_dec,
+                                const void* o_dec, const float* lse_dec, const void* do_dec,
+                                const void* q_enc, const void* o_enc, const float* lse_enc,
+                                const void* do_enc, void* dq_dec, void* dk_ctx, void* dv_ctx,
+                                void* dk_dec, void* dv_dec, void* dq_enc, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace e2d2_attn_denoise_step needs for these sizes (0 when the
  * call needs none; a NULL workspace is then accepted).  Host-only, no GPU needed. */
 size_t e2d2_attn_denoise_workspace_bytes(int dtype, int B, int Hq, int Hkv, int S, int d,

@@ -54,6 +54,8 @@ _SIGS = {
                                            _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "e2d2_kv_cache_append_varlen": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _ll, _ll, _vp, _vp,
                                          _vp]),
+    "e2d2_attn_train_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "e2d2_attn_train_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _f] + [_vp] * 19 + [_sz, _vp]),
     "e2d2_attn_tile_shape": (_i, [_i, _i, _i, _int_p, _int_p]),
     "e2d2_attn_count_tiles": (_i, [_i, _i, _i, _i, _i, _ll, _i, _i, _ull_p, _ull_p]),
 }
@@ -177,6 +179,52 @@ def e2d2_attn_train_fwd(q_dec, k_ctx, v_ctx, k_dec, v_dec, o_dec, S: int, lse_de
         _opt(q_enc, "q_enc", 4), _opt(o_enc, "o_enc", 4), _opt(lse_enc, "lse_enc", 3),
         _opt(tile_visits, "tile_visits", 1), _stream(q_dec))
     _check("e2d2_attn_train_fwd", st)
+
+
+def e2d2_attn_train_bwd_workspace_bytes(dtype: int, B: int, Hq: int, L: int, with_enc: bool) -> int:
+    return int(lib().e2d2_attn_train_bwd_workspace_bytes(dtype, B, Hq, L, 1 if with_enc else 0))
+
+
+def e2d2_attn_train_bwd(q_dec, k_ctx, v_ctx, k_dec, v_dec, o_dec, lse_dec, do_dec, S: int,
+                        dq_dec, dk_ctx, dv_ctx, dk_dec, dv_dec, workspace, q_enc=None,
+                        o_enc=None, lse_enc=None, do_enc=None, dq_enc=None, scale=None):
+    """Backward of e2d2_attn_train_fwd: writes dq_dec, dk_ctx, dv_ctx, dk_dec, dv_dec
+    (and dq_enc when q_enc is given) from the forward's o/lse and the upstream
+    gradients do_dec (do_enc).  ``workspace``: uint8 CUDA tensor of at least
+    e2d2_attn_train_bwd_workspace_bytes(...) bytes."""
+    B, Hq, L, d = q_dec.shape
+    Hkv = k_ctx.shape[1]
+    kv = (B, Hkv, L, d)
+    _same(q_dec.dtype, k_ctx, v_ctx, k_dec, v_dec, o_dec, do_dec, dq_dec, dk_ctx, dv_ctx, dk_dec, dv_dec)
+    for t in (o_dec, do_dec, dq_dec):
+        if t.shape != q_dec.shape:
+            raise ValueError("query-side tensors must be [B, Hq, L, d]")
+    for t in (k_ctx, v_ctx, k_dec, v_dec, dk_ctx, dv_ctx, dk_dec, dv_dec):
+        if tuple(t.shape) != kv:
+            raise ValueError("key-side tensors must be [B, Hkv, L, d]")
+    enc = [q_enc, o_enc, lse_enc, do_enc, dq_enc]
+    if q_enc is not None:
+        if any(t is None for t in enc):
+            raise ValueError("q_enc needs o_enc, lse_enc, do_enc and dq_enc")
+        _same(q_dec.dtype, q_enc, o_enc, do_enc, dq_enc)
+        for t in (q_enc, o_enc, do_enc, dq_enc):
+            if t.shape != q_dec.shape:
+                raise ValueError("encoder tensors must be [B, Hq, L, d]")
+    for t in (lse_dec, lse_enc):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (B, Hq, L)):
+            raise ValueError("lse must be float32 [B, Hq, L]")
+    ws_ptr = _dev(workspace, "workspace", workspace.dim())
+    ws_bytes = workspace.numel() * workspace.element_size()
+    opt = lambda t, n, nd=4: _opt(t, n, nd)
+    st = lib().e2d2_attn_train_bwd(
+        _dtype_code(q_dec), B, Hq, Hkv, L, d, S, _default_scale(d, scale),
+        _dev(q_dec, "q_dec"), _dev(k_ctx, "k_ctx"), _dev(v_ctx, "v_ctx"), _dev(k_dec, "k_dec"),
+        _dev(v_dec, "v_dec"), _dev(o_dec, "o_dec"), _dev(lse_dec, "lse_dec", 3),
+        _dev(do_dec, "do_dec"), opt(q_enc, "q_enc"), opt(o_enc, "o_enc"),
+        opt(lse_enc, "lse_enc", 3), opt(do_enc, "do_enc"), _dev(dq_dec, "dq_dec"),
+        _dev(dk_ctx, "dk_ctx"), _dev(dv_ctx, "dv_ctx"), _dev(dk_dec, "dk_dec"),
+        _dev(dv_dec, "dv_dec"), opt(dq_enc, "dq_enc"), ws_ptr, ws_bytes, _stream(q_dec))
+    _check("e2d2_attn_train_bwd", st)
 
 
 def e2d2_attn_denoise_workspace_bytes(dtype: int, B: int, Hq: int, Hkv: int, S: int, d: int,

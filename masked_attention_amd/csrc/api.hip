@@ -205,6 +205,81 @@ e2d2_status e2d2_attn_train_fwd(int dtype, int B, int Hq, int Hkv, int L, int d,
   return hip_status(e2d2::launch_attn_f32(p, d, s));
 }
 
+size_t e2d2_attn_train_bwd_workspace_bytes(int dtype, int B, int Hq, int L, int with_enc) {
+  if (dtype != E2D2_BF16 || B <= 0 || Hq <= 0 || L <= 0 || L > kMaxLen) return 0;
+  const size_t rows = (size_t)B * Hq * L;
+  // delta and lse*log2(e) per query row and kind, each array padded to 256 bytes
+  const size_t arr = (rows * sizeof(float) + 255) & ~(size_t)255;
+  return arr * 2 * (with_enc ? 2 : 1);
+}
+
+e2d2_status e2d2_attn_train_bwd(int dtype, int B, int Hq, int Hkv, int L, int d, int S,
+                                float scale, const void* q_dec, const void* k_ctx,
+                                const void* v_ctx, const void* k_dec, const void* v_dec,
+                                const void* o_dec, const float* lse_dec, const void* do_dec,
+                                const void* q_enc, const void* o_enc, const float* lse_enc,
+                                const void* do_enc, void* dq_dec, void* dk_ctx, void* dv_ctx,
+                                void* dk_dec, void* dv_dec, void* dq_enc, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  e2d2_status st = check_train_shape(dtype, B, Hq, Hkv, L, d, S, scale);
+  if (st != E2D2_OK) return st;
+  if (dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
+  if (!q_dec || !k_ctx || !v_ctx || !k_dec || !v_dec || !o_dec || !lse_dec || !do_dec ||
+      !dq_dec || !dk_ctx || !dv_ctx || !dk_dec || !dv_dec)
+    return E2D2_ERR_NULL;
+  const bool with_enc = q_enc != nullptr;
+  if (with_enc && (!o_enc || !lse_enc || !do_enc || !dq_enc)) return E2D2_ERR_NULL;
+  if (!with_enc && (o_enc || lse_enc || do_enc || dq_enc)) return E2D2_ERR_NULL;
+  const void* a16[] = {q_dec, k_ctx, v_ctx, k_dec, v_dec, o_dec, do_dec, dq_dec, dk_ctx, dv_ctx,
+                       dk_dec, dv_dec};
+  for (const void* x : a16)
+    if (!aligned16(x)) return E2D2_ERR_SHAPE;
+  if (!aligned4(lse_dec)) return E2D2_ERR_SHAPE;
+  if (with_enc && (!aligned16(q_enc) || !aligned16(o_enc) || !aligned16(do_enc) ||
+                   !aligned16(dq_enc) || !aligned4(lse_enc)))
+    return E2D2_ERR_SHAPE;
+  const size_t need = e2d2_attn_train_bwd_workspace_bytes(dtype, B, Hq, L, with_enc ? 1 : 0);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return E2D2_ERR_WORKSPACE;
+  const int rows_per_tile = e2d2::bwd_tile_rows();
+  if ((long long)cdiv(L, rows_per_tile) * B * Hq * 2 > INT32_MAX) return E2D2_ERR_SHAPE;
+  e2d2::BwdParams p = {};
+  p.q[0] = (const __bf16*)q_dec;
+  p.o[0] = (const __bf16*)o_dec;
+  p.dO[0] = (const __bf16*)do_dec;
+  p.lse[0] = lse_dec;
+  p.dq[0] = (__bf16*)dq_dec;
+  p.q[1] = (const __bf16*)q_enc;
+  p.o[1] = (const __bf16*)o_enc;
+  p.dO[1] = (const __bf16*)do_enc;
+  p.lse[1] = lse_enc;
+  p.dq[1] = (__bf16*)dq_enc;
+  p.k[0] = (const __bf16*)k_ctx;
+  p.v[0] = (const __bf16*)v_ctx;
+  p.k[1] = (const __bf16*)k_dec;
+  p.v[1] = (const __bf16*)v_dec;
+  p.dk[0] = (__bf16*)dk_ctx;
+  p.dv[0] = (__bf16*)dv_ctx;
+  p.dk[1] = (__bf16*)dk_dec;
+  p.dv[1] = (__bf16*)dv_dec;
+  const size_t rows = (size_t)B * Hq * L;
+  const size_t arr = (rows * sizeof(float) + 255) & ~(size_t)255;
+  char* ws = (char*)workspace;
+  p.delta[0] = (float*)ws;
+  p.lse2[0] = (float*)(ws + arr);
+  p.delta[1] = with_enc ? (float*)(ws + 2 * arr) : nullptr;
+  p.lse2[1] = with_enc ? (float*)(ws + 3 * arr) : nullptr;
+  p.kinds[0] = e2d2::kDec;
+  p.kinds[1] = e2d2::kEnc;
+  p.n_kinds = with_enc ? 2 : 1;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
+  p.n_qtiles = cdiv(L, rows_per_tile);
+  p.n_ktiles = cdiv(L, rows_per_tile);
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  return hip_status(e2d2::launch_train_bwd_bf16(p, d, (hipStream_t)stream));
+}
+
 size_t e2d2_attn_denoise_workspace_bytes(int dtype, int B, int Hq, int Hkv, int S, int d,
                                          long long cache_len) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || !head_dim_ok(d) || Hq % Hkv != 0 ||

@@ -67,7 +67,35 @@ struct DenoiseParams {
   unsigned long long* visits;
 };
 
+// Training backward, bf16.  Slot s (0: decoder, 1: encoder when n_kinds == 2) has
+// queries q[s], forward output o[s], its LSE lse[s], upstream gradient dO[s] and
+// query gradient dq[s]; key source 0 is (k[0], v[0]) (clean context, read by both
+// kinds), source 1 is (k[1], v[1]) (noised block, decoder only), with gradients
+// dk[src], dv[src].  delta[s], lse2[s]: fp32 [B][Hq][L] workspace rows.
+struct BwdParams {
+  const __bf16* q[2];
+  const __bf16* o[2];
+  const __bf16* dO[2];
+  const float* lse[2];
+  __bf16* dq[2];
+  const __bf16* k[2];
+  const __bf16* v[2];
+  __bf16* dk[2];
+  __bf16* dv[2];
+  float* delta[2];
+  float* lse2[2];
+  int kinds[2];
+  int n_kinds;
+  int B, Hq, Hkv, L, S;
+  int n_qtiles;  // query tiles of bwd_tile_rows() rows (dQ)
+  int n_ktiles;  // key tiles of bwd_tile_rows() keys per source (dK/dV)
+  float scale;
+  float c;       // scale * log2(e)
+};
+
 int train_tile_bm(int d);
+int bwd_tile_rows();
+hipError_t launch_train_bwd_bf16(const BwdParams& p, int d, hipStream_t stream);
 int train_tile_bn();
 constexpr int kF32TileBM = 64;
 constexpr int kF32TileBN = 64;

@@ -108,4 +108,24 @@ E2D2_HD int classify(int kind, int src, int r0, int r1, int S, int L, int C, int
   return (c.lo <= k0 && k1 <= c.hi) ? 2 : 1;
 }
 
+// ---- The transposed view, for the backward pass: which query rows allow key j.
+// By the same masks, every key allows one contiguous interval of query rows:
+//   ENC      (key j of the clean keys):    [start(j), L)        blk(i) >= blk(j)
+//   DEC src0 (clean context key j):        [start(j) + S, L)    blk(i) >  blk(j)
+//   DEC src1 (noised key j):               [start(j), end(j))   blk(i) == blk(j)
+// (clamped to [0, L]); both bounds are non-decreasing in j, so over keys k0..k1 the
+// union is [lo(k0), hi(k1)) and the rows every key allows are [lo(k1), hi(k0)).
+E2D2_HD Interval col_interval(int kind, int src, int j, int S, int L) {
+  const int st = block_start(j, S);
+  if (kind == kEnc) return {st, L};
+  if (src == 0) return {st + S < L ? st + S : L, L};
+  return {st, block_end(j, S, L)};
+}
+E2D2_HD Interval col_union(int kind, int src, int k0, int k1, int S, int L) {
+  return {col_interval(kind, src, k0, S, L).lo, col_interval(kind, src, k1, S, L).hi};
+}
+E2D2_HD Interval col_common(int kind, int src, int k0, int k1, int S, int L) {
+  return {col_interval(kind, src, k1, S, L).lo, col_interval(kind, src, k0, S, L).hi};
+}
+
 }  // namespace e2d2

@@ -181,3 +181,29 @@ def test_append_varlen_validation():
     assert f(m.BF16, 1, 1, 4, 64, 16, 16, None, 12, 16, 16, 16, None) == ERR_NULL
     assert f(m.BF16, 1, 1, 4, 64, 16, 16, 18, 12, 16, 16, 16, None) == ERR_SHAPE
     assert f(m.BF16, 1, 1, 4, 48, 16, 16, 16, 12, 16, 16, 16, None) == ERR_UNSUPPORTED
+
+
+def _bwd(**kw):
+    a = dict(dtype=m.BF16, B=1, Hq=2, Hkv=1, L=64, d=64, S=8, scale=0.125, q_dec=16, k_ctx=16,
+             v_ctx=16, k_dec=16, v_dec=16, o_dec=16, lse_dec=16, do_dec=16, q_enc=None,
+             o_enc=None, lse_enc=None, do_enc=None, dq_dec=16, dk_ctx=16, dv_ctx=16, dk_dec=16,
+             dv_dec=16, dq_enc=None, ws=16, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return m.lib().e2d2_attn_train_bwd(*a.values())
+
+
+def test_train_bwd_validation_returns_before_launch():
+    assert _bwd(lse_dec=None) == ERR_NULL
+    assert _bwd(dk_ctx=None) == ERR_NULL
+    assert _bwd(q_enc=16) == ERR_NULL                 # encoder query without its other tensors
+    assert _bwd(dq_enc=16) == ERR_NULL                # encoder output without its query
+    assert _bwd(dtype=m.F32) == ERR_UNSUPPORTED
+    assert _bwd(d=96) == ERR_UNSUPPORTED
+    assert _bwd(Hq=3, Hkv=2) == ERR_SHAPE
+    assert _bwd(do_dec=24) == ERR_SHAPE               # misaligned
+    assert _bwd(ws=None) == ERR_WORKSPACE
+    need = m.e2d2_attn_train_bwd_workspace_bytes(m.BF16, 1, 2, 64, True)
+    assert need >= 4 * 2 * 64 * 4
+    assert m.e2d2_attn_train_bwd_workspace_bytes(m.BF16, 1, 2, 64, False) * 2 == need
+    assert _bwd(q_enc=16, o_enc=16, lse_enc=16, do_enc=16, dq_enc=16, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert m.e2d2_attn_train_bwd_workspace_bytes(m.F32, 1, 2, 64, True) == 0

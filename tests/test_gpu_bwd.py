@@ -1,0 +1,125 @@
+"""GPU parity of the training backward (e2d2_attn_train_bwd) against the fp64 oracle's
+gradients (oracle.train_bwd).  The GPU gets its O and LSE from its own forward, as in
+training; the oracle derives everything from Q, K, V and the upstream gradients.
+
+Tolerance, per gradient tensor: |got - ref| <= 2e-2 * max(1, max |ref|).  The gradients
+are rounded to bf16 on output (2^-9 relative) and are built from bf16 P and dS
+operands, so their error scales with their magnitude; for tensors of magnitude <= 1 this
+is the forward's 2e-2 absolute bar.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import masked_attention_amd as m
+import oracle
+from helpers import TensorKind as K, host, scale_of
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["dq_dec", "dk_ctx", "dv_ctx", "dk_dec", "dv_dec", "dq_enc"]
+
+
+def say(msg):
+    print(msg, file=sys.__stderr__, flush=True)
+
+
+def check_grad(got, ref, what):
+    g = got.detach().double().cpu().numpy()
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite"
+    tol = 2e-2 * max(1.0, float(np.abs(r).max()))
+    err = np.abs(g - r)
+    if (err > tol).any():
+        idx = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{what}: {int((err > tol).sum())} elements out of tolerance {tol:.3g}; "
+                             f"max err {err.max():.3e} at {idx} (got {g[idx]}, ref {r[idx]})")
+    return float(err.max())
+
+
+def run_gpu(ins, S, with_enc):
+    """Forward then backward on the GPU; returns the gradient tensors (NAMES order)."""
+    q_dec, k_ctx, v_ctx, k_dec, v_dec, q_enc, do_dec, do_enc = [t.cuda() for t in ins]
+    B, Hq, L, d = q_dec.shape
+    o_dec, o_enc = torch.empty_like(q_dec), torch.empty_like(q_dec)
+    lse_dec = torch.empty((B, Hq, L), device="cuda")
+    lse_enc = torch.empty_like(lse_dec)
+    m.e2d2_attn_train_fwd(q_dec, k_ctx, v_ctx, k_dec, v_dec, o_dec, S, lse_dec=lse_dec,
+                          q_enc=q_enc if with_enc else None, o_enc=o_enc if with_enc else None,
+                          lse_enc=lse_enc if with_enc else None)
+    grads = [torch.full_like(t, float("nan")) for t in (q_dec, k_ctx, v_ctx, k_dec, v_dec, q_dec)]
+    ws = torch.empty(m.e2d2_attn_train_bwd_workspace_bytes(m.BF16, B, Hq, L, with_enc),
+                     dtype=torch.uint8, device="cuda")
+    enc = dict(q_enc=q_enc, o_enc=o_enc, lse_enc=lse_enc, do_enc=do_enc, dq_enc=grads[5]) if with_enc else {}
+    m.e2d2_attn_train_bwd(q_dec, k_ctx, v_ctx, k_dec, v_dec, o_dec, lse_dec, do_dec, S,
+                          grads[0], grads[1], grads[2], grads[3], grads[4], ws, **enc)
+    torch.cuda.synchronize()
+    return grads if with_enc else grads[:5]
+
+
+def inputs(B, Hq, Hkv, L, d, seed):
+    q = (B, Hq, L, d)
+    kv = (B, Hkv, L, d)
+    return [host(q, seed, K.Q_DEC, "bf16"), host(kv, seed, K.K_CTX, "bf16"),
+            host(kv, seed, K.V_CTX, "bf16"), host(kv, seed, K.K_DEC, "bf16"),
+            host(kv, seed, K.V_DEC, "bf16"), host(q, seed, K.Q_ENC, "bf16"),
+            host(q, seed, K.DO_DEC, "bf16"), host(q, seed, K.DO_ENC, "bf16")]
+
+
+@pytest.mark.parametrize("with_enc", [True, False])
+@pytest.mark.parametrize("B,Hq,Hkv,L,S,d", [
+    (1, 2, 1, 64, 8, 64),      # tiles of the workload shape's head dim
+    (2, 4, 2, 100, 7, 32),     # ragged last block and tile, grouped heads
+    (1, 2, 2, 130, 16, 128),   # several key/query tiles, ragged, d = 128
+    (1, 2, 1, 40, 1, 64),      # block size 1 (causal)
+    (1, 1, 1, 72, 72, 64),     # block size L (full attention)
+    (1, 4, 1, 200, 33, 64),    # blocks straddling tiles, 4 heads per kv head
+])
+def test_bwd_matches_oracle(B, Hq, Hkv, L, S, d, with_enc):
+    seed = 0xE2D2B000 + L + S + d
+    say(f"[bwd] B{B} Hq{Hq} Hkv{Hkv} L{L} S{S} d{d} enc={with_enc}")
+    ins = inputs(B, Hq, Hkv, L, d, seed)
+    got = run_gpu(ins, S, with_enc)
+    ref = oracle.train_bwd(*ins[:5], S, scale_of(d), ins[6], q_enc=ins[5] if with_enc else None,
+                           do_enc=ins[7] if with_enc else None)
+    for name, g, r in zip(NAMES, got, ref):
+        check_grad(g, r, name)
+
+
+def test_bwd_training_workload_sampled_heads():
+    # B8 H16 d64 L1024 S16 (the training forward's workload), all kv heads computed on
+    # the GPU, three (batch, kv head) groups checked against the oracle.
+    B, Hq, Hkv, L, S, d = 8, 16, 16, 1024, 16, 64
+    seed = 0xE2D2B100
+    say(f"[bwd] full B{B} H{Hq} L{L} S{S} d{d}")
+    ins = inputs(B, Hq, Hkv, L, d, seed)
+    got = run_gpu(ins, S, True)
+    heads = [(0, 0), (3, 7), (7, 15)]
+    ref = oracle.train_bwd(*ins[:5], S, scale_of(d), ins[6], q_enc=ins[5], do_enc=ins[7],
+                           kv_heads=heads)
+    for b, h in heads:
+        for name, g, r in zip(NAMES, got, ref):
+            check_grad(g[b, h], r[b, h], f"{name}[{b},{h}]")
+
+
+def test_bwd_grouped_heads_d128_longer():
+    B, Hq, Hkv, L, S, d = 1, 4, 2, 1024, 64, 128
+    seed = 0xE2D2B200
+    say(f"[bwd] B{B} Hq{Hq}/{Hkv} L{L} S{S} d{d}")
+    ins = inputs(B, Hq, Hkv, L, d, seed)
+    got = run_gpu(ins, S, True)
+    ref = oracle.train_bwd(*ins[:5], S, scale_of(d), ins[6], q_enc=ins[5], do_enc=ins[7])
+    for name, g, r in zip(NAMES, got, ref):
+        check_grad(g, r, name)
+
+
+def test_bwd_is_deterministic():
+    B, Hq, Hkv, L, S, d = 2, 4, 2, 300, 12, 64
+    ins = inputs(B, Hq, Hkv, L, d, 0xE2D2B300)
+    a = run_gpu(ins, S, True)
+    b = run_gpu(ins, S, True)
+    for name, x, y in zip(NAMES, a, b):
+        assert torch.equal(x, y), name
