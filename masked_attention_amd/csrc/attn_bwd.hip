@@ -11,14 +11,15 @@
 // For one (batch, query head), with p_ij = exp(s_ij - lse_i) on allowed pairs and the
 // upstream gradient do_i:  dv_j = sum_i p_ij do_i,  dp_ij = <do_i, v_j>,
 // ds_ij = p_ij (dp_ij - delta_i) with delta_i = <do_i, o_i>,  dq_i = scale sum_j ds_ij
-// k_j,  dk_j = scale sum_i ds_ij q_i.  Three launches, no atomics (deterministic):
-//   1. delta: delta_i and lse_i * log2(e) per query row, fp32, into the workspace.
-//   2. dQ: query-stationary, the forward's schedule: a workgroup owns 128 query rows
+// k_j,  dk_j = scale sum_i ds_ij q_i.  Two launches, no atomics (deterministic):
+//   1. dQ: query-stationary, the forward's schedule: a workgroup owns 128 query rows
 //      of one (batch, query head, kind) and walks the key tiles holding an allowed
-//      pair.  Per 32x32 block: S^T = K Q^T and dP^T = V dO^T on the MFMA (K and V
-//      rows from LDS, Q and dO in registers), P^T = 2^(S^T c - lse), dS^T = P^T (dP^T -
-//      delta), then dQ^T += K^T dS^T with K^T from the transposing LDS read.
-//   3. dK/dV: key-stationary: a workgroup owns 128 keys of one (batch, kv head, key
+//      pair.  It first forms delta_i = <do_i, o_i> and lse_i * log2(e) of its rows
+//      (fp32, also written to the workspace for launch 2).  Per 32x32 block: S^T =
+//      K Q^T and dP^T = V dO^T on the MFMA (K and V rows from LDS, Q and dO in
+//      registers), P^T = 2^(S^T c - lse), dS^T = P^T (dP^T - delta), then dQ^T += K^T
+//      dS^T with K^T from the transposing LDS read.
+//   2. dK/dV: key-stationary: a workgroup owns 128 keys of one (batch, kv head, key
 //      source) and walks the 64-row query tiles that allow any of them -- every query
 //      head of the group, and for the clean keys both the encoder's and the decoder's
 //      queries -- so each key's gradient is summed in one place.  Per 32x32 block:
@@ -38,29 +39,6 @@ constexpr int kTK = 64;     // keys per K/V tile (dQ) and query rows per Q/dO ti
 constexpr int kRows = 128;  // query rows (dQ) or keys (dK/dV) per workgroup: 4 waves x 32
 constexpr int kWaves = 4;
 
-// ---- 1. delta_i = <do_i, o_i> and lse_i * log2(e), one row per thread
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  const long long rows = (long long)p.B * p.Hq * p.L;
-  for (long long r = (long long)blockIdx.x * 256 + threadIdx.x; r < rows * p.n_kinds;
-       r += (long long)gridDim.x * 256) {
-    const bool s1 = r >= rows;
-    const long long rr = s1 ? r - rows : r;
-    const __bf16* o = (s1 ? p.o[1] : p.o[0]) + rr * D;
-    const __bf16* g = (s1 ? p.dO[1] : p.dO[0]) + rr * D;
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < D; c += 8) {
-      const bf16x8 a = *(const bf16x8*)(o + c);
-      const bf16x8 b = *(const bf16x8*)(g + c);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf((float)a[j], (float)b[j], acc);
-    }
-    (s1 ? p.delta[1] : p.delta[0])[rr] = acc;
-    (s1 ? p.lse2[1] : p.lse2[0])[rr] = (s1 ? p.lse[1] : p.lse[0])[rr] * kLog2e;
-  }
-}
-
 template <int D>
 struct BwdGeo {
   static constexpr int NC = D / 16;
@@ -69,7 +47,7 @@ struct BwdGeo {
   static constexpr int STAGE = 2 * TILE;
 };
 
-// ---- 2. dQ
+// ---- 1. dQ (and delta, lse * log2(e))
 template <int D>
 __global__ __launch_bounds__(256, D > 64 ? 2 : 3) void bwd_dq_kernel(BwdParams p) {
   using G = BwdGeo<D>;
@@ -171,9 +149,30 @@ __global__ __launch_bounds__(256, D > 64 ? 2 : 3) void bwd_dq_kernel(BwdParams p
       df[cc] = *(const bf16x8*)(drow + cc * 16);
     }
   }
-  // rows past L: lse = +inf makes every p zero
-  const float lse2 = row_ok ? (slot ? p.lse2[1] : p.lse2[0])[q_row] : INFINITY;
-  const float dlt = row_ok ? (slot ? p.delta[1] : p.delta[0])[q_row] : 0.f;
+  // delta = <dO, O> of this lane's row (the pair of lanes l, l^32 holds it in halves),
+  // and lse * log2(e); both also go to the workspace for the dK/dV kernel.  Rows past
+  // L: lse = +inf makes every p zero.
+  float dlt, lse2;
+  {
+    const __bf16* orow = (slot ? p.o[1] : p.o[0]) + q_row * D + ((lane >> 5) << 3);
+    float part = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const bf16x8 ov = *(const bf16x8*)(orow + cc * 16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part = fmaf((float)ov[j], (float)df[cc][j], part);
+    }
+    dlt = pair_sum(part);
+    lse2 = (slot ? p.lse[1] : p.lse[0])[q_row] * kLog2e;
+    if (row_ok && lane < 32) {
+      (slot ? p.delta[1] : p.delta[0])[q_row] = dlt;
+      (slot ? p.lse2[1] : p.lse2[0])[q_row] = lse2;
+    }
+    if (!row_ok) {
+      dlt = 0.f;
+      lse2 = INFINITY;
+    }
+  }
   uint32_t koff[NC];
   k_offsets<D>(lane, koff);
   uint32_t offA[NDB], offB[NDB];
@@ -259,7 +258,7 @@ __global__ __launch_bounds__(256, D > 64 ? 2 : 3) void bwd_dq_kernel(BwdParams p
   }
 }
 
-// ---- 3. dK / dV
+// ---- 2. dK / dV
 //
 // Query-tile stream of a key workgroup: for each kind slot reading this key source,
 // for each query head of the kv head's group, the 64-row query tiles [qt0, qt1) that
@@ -394,32 +393,40 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
     dv[db] = zero16();
   }
 
+  // rows of a 32-row block (KB) of the tile at LDS offset BASE, times the registers w:
+  // the S = Q K^T (or dP = dO V^T) block; operands read half at a time (registers)
+  auto rows_dot = [&](auto kbc, auto basec, const bf16x8 (&w)[NC]) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kbc)::value, BASE = decltype(basec)::value;
+    f32x16 acc = zero16();
+    if constexpr (NC >= 4) {
+      constexpr int H = NC / 2;
+      bf16x8 a[H];
+      kread_part<D, KB, BASE, 0, H>(lds0, koff, a);
+#pragma unroll
+      for (int cc = 0; cc < H; ++cc) acc = mfma32(a[cc], w[cc], acc);
+      kread_part<D, KB, BASE, H, H>(lds0, koff, a);
+#pragma unroll
+      for (int cc = 0; cc < H; ++cc) acc = mfma32(a[cc], w[H + cc], acc);
+    } else {
+      bf16x8 a[NC];
+      kread_block<D, KB, BASE>(lds0, koff, a);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) acc = mfma32(a[cc], w[cc], acc);
+    }
+    return acc;
+  };
   // query block qb (32 rows) of the tile in stage STG, stream slot ss, query tile qt
-  auto block = [&](int qb, int cl, int ss, int qt, auto stg) __attribute__((always_inline)) {
+  auto block = [&](auto qbc, int cl, int ss, int qt, auto stg) __attribute__((always_inline)) {
+    constexpr int QB = decltype(qbc)::value;
     constexpr int QOFF = decltype(stg)::value * STAGE_B;
     constexpr int DOFF = QOFF + TILE * 2;
     constexpr int SOFF = QOFF + 2 * TILE * 2;
-    bf16x8 af[NC];
-    if (qb == 0) kread_block<D, 0, QOFF>(lds0, koff, af);
-    else kread_block<D, 1, QOFF>(lds0, koff, af);
-    f32x16 s = zero16();
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) s = mfma32(af[cc], kf[cc], s);
-    if (qb == 0) kread_block<D, 0, DOFF>(lds0, koff, af);
-    else kread_block<D, 1, DOFF>(lds0, koff, af);
-    f32x16 dp = zero16();
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) dp = mfma32(af[cc], vf[cc], dp);
-    // this lane's 16 query rows: qb * 32 + 8 (j / 4) + 4 (lane / 32) + j % 4
+    f32x16 s = rows_dot(IntC<QB>{}, IntC<QOFF>{}, kf);
+    const f32x16 dp = rows_dot(IntC<QB>{}, IntC<DOFF>{}, vf);
+    // this lane's 16 query rows: QB * 32 + 8 (j / 4) + 4 (lane / 32) + j % 4
     const float E2D2_LDS* lse_t = (const float E2D2_LDS*)(smem_raw + SOFF);
     const float E2D2_LDS* dlt_t = lse_t + 64;
-    const int rb = qb * 32 + ((lane >> 5) << 2);
-    f32x4 l4[4], d4[4];
-#pragma unroll
-    for (int jg = 0; jg < 4; ++jg) {
-      l4[jg] = *(const f32x4 E2D2_LDS*)(lse_t + rb + 8 * jg);
-      d4[jg] = *(const f32x4 E2D2_LDS*)(dlt_t + rb + 8 * jg);
-    }
+    const int rb = QB * 32 + ((lane >> 5) << 2);
     if (cl == 1) {
       const Interval r = ss ? civ[1] : civ[0];
       const int q_r = qt * kTK + rb;
@@ -429,33 +436,35 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
         if (q < r.lo || q >= r.hi) s[j] = -INFINITY;
       }
     }
-    bf16x8 pb[2], dsb[2];
+    // per 16-row half h: P and dS of registers 8h .. 8h+7, then dV^T += dO^T P and
+    // dK^T += Q^T dS for those 16 query rows
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const f32x4 l0 = *(const f32x4 E2D2_LDS*)(lse_t + rb + 16 * h);
+      const f32x4 l1 = *(const f32x4 E2D2_LDS*)(lse_t + rb + 16 * h + 8);
+      const f32x4 d0 = *(const f32x4 E2D2_LDS*)(dlt_t + rb + 16 * h);
+      const f32x4 d1 = *(const f32x4 E2D2_LDS*)(dlt_t + rb + 16 * h + 8);
       float e[8], f[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int jj = 8 * h + j;
-        const float pj = fast_exp2(fmaf(s[jj], c, -l4[jj >> 2][jj & 3]));
+        const float lj = j < 4 ? l0[j] : l1[j - 4];
+        const float dj = j < 4 ? d0[j] : d1[j - 4];
+        const float pj = fast_exp2(fmaf(s[8 * h + j], c, -lj));
         e[j] = pj;
-        f[j] = pj * (dp[jj] - d4[jj >> 2][jj & 3]);
+        f[j] = pj * (dp[8 * h + j] - dj);
       }
-      pb[h] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      dsb[h] = to_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+      const bf16x8 pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      const bf16x8 dsb = to_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+      bf16x8 tf[NDB];
+      if (h == 0) read_vt_half32<D, DOFF + QB * 64 * D, 0>(lds0, offA, offB, tf);
+      else read_vt_half32<D, DOFF + QB * 64 * D, 1>(lds0, offA, offB, tf);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dv[db] = mfma32(tf[db], pb, dv[db]);
+      if (h == 0) read_vt_half32<D, QOFF + QB * 64 * D, 0>(lds0, offA, offB, tf);
+      else read_vt_half32<D, QOFF + QB * 64 * D, 1>(lds0, offA, offB, tf);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dk[db] = mfma32(tf[db], dsb, dk[db]);
     }
-    bf16x8 tf[2][NDB];
-    if (qb == 0) read_vt_tile32<D, DOFF>(lds0, offA, offB, tf);
-    else read_vt_tile32<D, DOFF + 64 * D>(lds0, offA, offB, tf);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) dv[db] = mfma32(tf[h][db], pb[h], dv[db]);
-    if (qb == 0) read_vt_tile32<D, QOFF>(lds0, offA, offB, tf);
-    else read_vt_tile32<D, QOFF + 64 * D>(lds0, offA, offB, tf);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) dk[db] = mfma32(tf[h][db], dsb[h], dk[db]);
   };
   auto tile = [&](int u, auto stg) __attribute__((always_inline)) {
     wait_vmem<0>();   // tile u is the only load in flight
@@ -474,7 +483,10 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
       if (r1 <= un.lo || r0 >= un.hi || r1 <= r0) cl = 0;
       else if (cm.lo <= r0 && r1 <= cm.hi && r1 - r0 == 32 && kw1 - kw0 == 32) cl = 2;
       else cl = 1;
-      if (cl) block(qb, cl, ss, qt, stg);
+      if (cl) {
+        if (qb == 0) block(IntC<0>{}, cl, ss, qt, stg);
+        else block(IntC<1>{}, cl, ss, qt, stg);
+      }
     }
   };
   for (int u = 0; u < ntot; u += 2) {
@@ -506,14 +518,6 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   using G = BwdGeo<D>;
-  {
-    const long long rows = (long long)p.B * p.Hq * p.L * p.n_kinds;
-    long long blocks = (rows + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   {
     const size_t smem = 2 * (size_t)G::STAGE * sizeof(__bf16);
     if (smem > 64 * 1024) {

@@ -296,7 +296,49 @@ __device__ __forceinline__ void tr_reads(const uint32_t (&a)[8], long (&o)[16]) 
       : "memory");
 }
 
-// Batched 16-byte LDS reads (the K operands of S^T = K Q^T), in one asm block that
+// Transposing reads at one offset: o[i] = 8 bytes at a[i] + O (N in {2, 4, 8}).
+template <int O>
+__device__ __forceinline__ void tr_reads1(const uint32_t (&a)[2], long (&o)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2 offset:%4\n\t"
+      "ds_read_b64_tr_b16 %1, %3 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1])
+      : "v"(a[0]), "v"(a[1]), "i"(O)
+      : "memory");
+}
+template <int O>
+__device__ __forceinline__ void tr_reads1(const uint32_t (&a)[4], long (&o)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(O)
+      : "memory");
+}
+template <int O>
+__device__ __forceinline__ void tr_reads1(const uint32_t (&a)[8], long (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+        "v"(a[7]), "i"(O)
+      : "memory");
+}
+
+// Batched 16-byte LDS reads (the K operands of S^T = K Q^T), in one asm block that// Batched 16-byte LDS reads (the K operands of S^T = K Q^T), in one asm block that
 // waits for them, so one LDS round trip covers a whole batch of MFMAs instead of one
 // each.  kreadN<OFF>: o[i] = 16 bytes at a[i] + OFF.
 template <int OFF>
@@ -338,6 +380,22 @@ __device__ __forceinline__ void kread2(const uint32_t (&a)[2], bf16x8 (&o)[2]) {
       : "=&v"(o[0]), "=&v"(o[1])
       : "v"(a[0]), "v"(a[1]), "i"(OFF)
       : "memory");
+}
+
+// Part of a 32-row block's operands: o[i] = the 16 bytes kread_block would put in
+// kf[C0 + i], for i < CN (CN in {2, 4, 8}); lets a caller hold half the operands.
+template <int D, int KB, int BASE, int C0, int CN>
+__device__ __forceinline__ void kread_part(uint32_t kbase, const uint32_t (&koff)[D / 16],
+                                           bf16x8 (&o)[CN]) {
+  constexpr int OFF = BASE + KB * 64 * D;
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field is 16 bits");
+  static_assert(C0 + CN <= D / 16, "operand range");
+  uint32_t a[CN];
+#pragma unroll
+  for (int i = 0; i < CN; ++i) a[i] = kbase + koff[C0 + i];
+  if constexpr (CN == 8) kread8<OFF>(a, o);
+  else if constexpr (CN == 4) kread4<OFF>(a, o);
+  else kread2<OFF>(a, o);
 }
 
 // S^T = K Q^T for the 32-key blocks of a K tile at LDS byte address kbase whose mask
@@ -494,7 +552,27 @@ struct IntC {
   static constexpr int value = N;
 };
 
-// LDS byte address of an LDS pointer.
+// One 16-row half h of read_vt_tile32's operands: vf[db] == read_vt_tile32's vf[h][db].
+template <int D, int BASE, int H>
+__device__ __forceinline__ void read_vt_half32(uint32_t vbase, const uint32_t (&offA)[D / 32],
+                                               const uint32_t (&offB)[D / 32],
+                                               bf16x8 (&vf)[D / 32]) {
+  constexpr int NDB = D / 32;
+  constexpr int O = BASE + H * 32 * D;
+  static_assert(O >= 0 && O < 65536, "LDS offset field is 16 bits");
+  uint32_t a[2 * NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    a[2 * db] = vbase + offA[db];
+    a[2 * db + 1] = vbase + offB[db];
+  }
+  long o[2 * NDB];
+  tr_reads1<O>(a, o);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) vf[db] = join_bf16(o[2 * db], o[2 * db + 1]);
+}
+
+// LDS byte address of an LDS pointer.// LDS byte address of an LDS pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void E2D2_LDS* p) {
   return (uint32_t)(uintptr_t)p;
 }
