@@ -206,6 +206,48 @@ def bench_train_bwd(B, Hq, Hkv, L, S, d, steps, seed):
                 frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4), useful_flop=useful)
 
 
+def bench_layer_split(B, H, L, S, d, steps, seed):
+    """Per-layer attention cost of a decoder-only block-diffusion layer (one fused call
+    over the 2L tokens: decoder half + encoder half) against an E2D2 encoder layer
+    (encoder half alone) and an E2D2 decoder layer (decoder half alone), each timed
+    from a HIP graph of `steps` launches."""
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+
+    def fill(kind):
+        t = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=dev)
+        device_fill(t, seed, tensor_id(kind))
+        return t
+
+    qd, qe, kc, vc, kd, vd = (fill(k) for k in (K.Q_DEC, K.Q_ENC, K.K_CTX, K.V_CTX, K.K_DEC, K.V_DEC))
+    od, oe = torch.empty_like(qd), torch.empty_like(qe)
+    ld = torch.empty((B, H, L), device=dev)
+    le = torch.empty_like(ld)
+    calls = {
+        "bd3lm_layer": lambda: m.e2d2_attn_train_fwd(qd, kc, vc, kd, vd, od, S, lse_dec=ld,
+                                                     q_enc=qe, o_enc=oe, lse_enc=le),
+        "e2d2_encoder_layer": lambda: m.e2d2_attn_encoder_blockcausal(qe, kc, vc, oe, S, lse=le),
+        "e2d2_decoder_layer": lambda: m.e2d2_attn_train_fwd(qd, kc, vc, kd, vd, od, S, lse_dec=ld),
+    }
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        g = graph_of(fn, steps)
+        clock_warmup(g.replay)
+        total, _ = timed_launches(g.replay, 1, stream)
+        out[name + "_us"] = round(total / steps * 1e3, 2)
+    out["workload"] = f"attention per layer, B{B} H{H} d{d} L{L} S{S} bf16"
+    out["bd3lm_over_e2d2_mean_layer"] = round(
+        out["bd3lm_layer_us"] / ((out["e2d2_encoder_layer_us"] + out["e2d2_decoder_layer_us"]) / 2), 3)
+    return out
+
+
 def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
     import torch
 
@@ -402,7 +444,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["all", "train", "bwd", "denoise", "long", "nearar", "copycal"],
+    ap.add_argument("--only", choices=["all", "train", "bwd", "layers", "denoise", "long", "nearar",
+                                       "copycal"],
                     default="all",
                     help="restrict the run (profiling); 'copycal' runs only a plain 1 GiB "
                          "device copy, the reference for scaling HBM byte counters")
@@ -443,6 +486,9 @@ def main():
         for k in ("train_bwd", "long_train_bwd"):
             print(f"[bench] {k}: {out[k]['ms_per_step'] * 1e3:.1f} us, {out[k]['tflops']} TFLOP/s",
                   file=sys.stderr, flush=True)
+    if args.only in ("all", "layers"):
+        out["layer_split"] = bench_layer_split(8, 16, 1024, 16, 64, args.steps, 0xE2D20002)
+        print(f"[bench] layer split: {out['layer_split']}", file=sys.stderr, flush=True)
     if args.only in ("all", "long"):
         lt = bench_train(2, 16, 8, 8192, 64, 128, max(3, args.steps // 10), 2, 0xE2D20004)
         out["long_train"] = dict(

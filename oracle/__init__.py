@@ -19,6 +19,7 @@ from .masks import (  # noqa: F401
     encoder_mask,
     decoder_mask,
     denoise_mask,
+    bd3lm_mask,
     count_pairs,
     count_tiles,
 )
@@ -28,6 +29,7 @@ from .attention import (  # noqa: F401
     decoder_fused,
     train_fwd,
     denoise_step,
+    bd3lm_layer,
     kv_cache_append,
 )
 from .backward import (  # noqa: F401

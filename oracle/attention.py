@@ -30,7 +30,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .masks import decoder_mask, denoise_mask, encoder_mask
+from .masks import bd3lm_mask, decoder_mask, denoise_mask, encoder_mask
 
 _ROW_SLAB = 512
 
@@ -140,6 +140,24 @@ def train_fwd(q_dec, k_ctx, v_ctx, k_dec, v_dec, S: int, scale, q_enc=None, rows
         return o_dec, lse_dec, None, None
     o_enc, lse_enc = encoder_blockcausal(q_enc, k_ctx, v_ctx, S, scale, rows, heads)
     return o_dec, lse_dec, o_enc, lse_enc
+
+
+def bd3lm_layer(q, k, v, S: int, scale, heads=None):
+    """Attention of one decoder-only block-diffusion layer over 2L tokens [noised |
+    clean] with the explicit 2L x 2L mask (masks.bd3lm_mask): q, k, v [B, H*, 2L, d]
+    (query heads Hq, kv heads Hkv).  Returns o [B, Hq, 2L, d], lse [B, Hq, 2L]."""
+    B, Hq, L2, d = q.shape
+    Hkv = k.shape[1]
+    if L2 % 2:
+        raise ValueError("the sequence must hold 2L tokens")
+    mask = bd3lm_mask(L2 // 2, S)
+    o = np.full((B, Hq, L2, v.shape[3]), np.nan)
+    lse = np.full((B, Hq, L2), np.nan)
+    for b, hq in (heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]):
+        hk = _kv_head(hq, Hq, Hkv)
+        o[b, hq], lse[b, hq] = _run_rows(_f64(q[b, hq]), _f64(k[b, hk]), _f64(v[b, hk]),
+                                         lambda r: mask[r], np.arange(L2), scale)
+    return o, lse
 
 
 def denoise_step(q_blk, k_cache, v_cache, cache_len: int, k_blk, v_blk, scale, heads=None):

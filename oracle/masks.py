@@ -49,6 +49,21 @@ def decoder_mask(L: int, S: int) -> np.ndarray:
     return np.concatenate([clean, noised], axis=1)
 
 
+def bd3lm_mask(L: int, S: int) -> np.ndarray:
+    """[2L, 2L] bool of a decoder-only block-diffusion layer over the sequence
+    [noised 0..L-1 | clean 0..L-1] ([Notes] 背景与动机: such a model processes the whole
+    clean sequence and the whole noised sequence, 2L tokens, in one stack; FLOPs table,
+    BD3LM row).  Noised query i (block b) may attend noised key j iff block(j) == b and
+    clean key j iff block(j) < b; clean query i may attend clean key j iff block(j) <= b
+    and no noised key (the clean stream must not see the noise)."""
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    bi, bj = block_of(i, S), block_of(j, S)
+    noised_rows = np.concatenate([bj == bi, bj < bi], axis=1)
+    clean_rows = np.concatenate([np.zeros((L, L), dtype=bool), bj <= bi], axis=1)
+    return np.concatenate([noised_rows, clean_rows], axis=0)
+
+
 def denoise_mask(S: int, C: int) -> np.ndarray:
     """[S, C+S] bool over keys [cache 0..C-1 | own block 0..S-1]: all allowed."""
     return np.ones((S, C + S), dtype=bool)

@@ -183,3 +183,32 @@ def test_mask_structure_is_exact(L, S, d, dtype):
     assert np.array_equal(dec, oracle.decoder_mask(L, S))
     assert np.array_equal(ce, oracle.encoder_mask(L, S).sum(1))
     assert np.array_equal(cd, oracle.decoder_mask(L, S).sum(1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bd3lm_single_stack_layer_via_fused_call(dtype):
+    # A decoder-only block-diffusion layer over 2L tokens [noised | clean] (the FLOPs
+    # table's BD3LM row) is one fused call on its halves: noised queries as the decoder
+    # (clean keys as context, own-block noised keys), clean queries as the encoder.
+    # Checked against the oracle's explicit 2L x 2L mask.
+    B, Hq, Hkv, L, S, d = 2, 4, 2, 96, 16, 64
+    seed = 0xE2D2BD30
+    say(f"[bd3lm] B{B} Hq{Hq}/{Hkv} 2L={2 * L} S{S} d{d} {dtype}")
+    q = host((B, Hq, 2 * L, d), seed, K.Q_DEC, dtype)
+    k = host((B, Hkv, 2 * L, d), seed, K.K_CTX, dtype)
+    v = host((B, Hkv, 2 * L, d), seed, K.V_CTX, dtype)
+    half = lambda t, i: t[:, :, i * L:(i + 1) * L].contiguous().cuda()
+    od = torch.empty((B, Hq, L, d), dtype=TORCH_DT[dtype], device="cuda")
+    oe = torch.empty_like(od)
+    ld = torch.empty((B, Hq, L), device="cuda")
+    le = torch.empty_like(ld)
+    m.e2d2_attn_train_fwd(half(q, 0), half(k, 1), half(v, 1), half(k, 0), half(v, 0), od, S,
+                          lse_dec=ld, q_enc=half(q, 1), o_enc=oe, lse_enc=le)
+    torch.cuda.synchronize()
+    ro, rl = oracle.bd3lm_layer(q, k, v, S, scale_of(d))
+    for b in range(B):
+        for h in range(Hq):
+            check(od[b, h], ro[b, h, :L], dtype, f"noised o[{b},{h}]")
+            check(oe[b, h], ro[b, h, L:], dtype, f"clean o[{b},{h}]")
+            check(ld[b, h], rl[b, h, :L], dtype, f"noised lse[{b},{h}]")
+            check(le[b, h], rl[b, h, L:], dtype, f"clean lse[{b},{h}]")

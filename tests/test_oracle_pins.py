@@ -384,3 +384,42 @@ def test_synth_inputs_are_reproducible_and_sliceable():
     assert abs(x.mean()) < 5e-3 and abs(x.var() - 1) < 5e-3
     assert not torch.equal(host_tensor(5, tensor_id(TensorKind.Q_BLK, step=1), (1, 1, 4, 8), "f32"),
                            host_tensor(5, tensor_id(TensorKind.Q_BLK, step=2), (1, 1, 4, 8), "f32"))
+
+
+@pytest.mark.parametrize("L,S", [(L, S) for L in range(1, 41, 3) for S in (1, 2, 4, 5, 8) if S <= L])
+def test_bd3lm_pair_count_is_twice_each_e2d2_mask(L, S):
+    # FLOPs table: a decoder-only block-diffusion layer costs 4ND(L^2 + LS) attention
+    # flops, an E2D2 encoder or decoder layer 4ND(L^2 + LS)/2: twice the pairs per layer.
+    m = oracle.bd3lm_mask(L, S)
+    n_bd = oracle.count_pairs(m)
+    assert n_bd == oracle.count_pairs(oracle.encoder_mask(L, S)) + oracle.count_pairs(oracle.decoder_mask(L, S))
+    if L % S == 0:
+        assert n_bd == L * L + L * S
+
+
+def test_bd3lm_block_size_one_and_L():
+    # S = 1: clean half is causal attention and noised tokens see strictly earlier
+    # clean tokens plus themselves; S = L: one block, noised tokens see only noised.
+    L = 6
+    m1 = oracle.bd3lm_mask(L, 1)
+    assert np.array_equal(m1[L:, L:], np.tril(np.ones((L, L), dtype=bool)))
+    assert np.array_equal(m1[:L, :L], np.eye(L, dtype=bool))
+    assert np.array_equal(m1[:L, L:], np.tril(np.ones((L, L), dtype=bool), -1))
+    mL = oracle.bd3lm_mask(L, L)
+    assert mL[:L, :L].all() and not mL[:L, L:].any() and mL[L:, L:].all() and not mL[L:, :L].any()
+
+
+def test_bd3lm_layer_is_the_fused_e2d2_call_on_its_halves():
+    # Splitting the 2L tokens into [noised | clean] halves, the single-stack layer equals
+    # the decoder attention of the noised half (clean keys as context) and the encoder
+    # attention of the clean half.
+    B, H, L, S, d = 1, 2, 10, 3, 4
+    g = lambda kind: host_tensor(0xBD3, tensor_id(kind), (B, H, 2 * L, d), "f32")
+    q, k, v = g(TensorKind.Q_DEC), g(TensorKind.K_CTX), g(TensorKind.V_CTX)
+    o, lse = oracle.bd3lm_layer(q, k, v, S, 0.4)
+    od, ld, oe, le = oracle.train_fwd(q[:, :, :L], k[:, :, L:], v[:, :, L:], k[:, :, :L],
+                                      v[:, :, :L], S, 0.4, q_enc=q[:, :, L:])
+    np.testing.assert_allclose(o[:, :, :L], od, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o[:, :, L:], oe, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[:, :, :L], ld, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[:, :, L:], le, rtol=1e-12, atol=1e-12)
