@@ -36,3 +36,7 @@ from .backward import (  # noqa: F401
     masked_softmax_attention_grad,
     train_bwd,
 )
+from .layer import (  # noqa: F401
+    round_bf16,
+    decoder_layer_denoise,
+)

@@ -16,4 +16,7 @@ from .gen import (  # noqa: F401
     host_tensor,
     device_fill,
     device_available,
+    draw_view,
+    host_draw,
+    device_draw,
 )

@@ -52,6 +52,9 @@ class TensorKind(enum.IntEnum):
     PROBE = 14
     DO_DEC = 15   # upstream gradient of the decoder attention output (backward pass)
     DO_ENC = 16   # upstream gradient of the encoder attention output
+    X_BLK = 17    # hidden states of a block's noised tokens entering a decoder layer
+    W_QKV = 18    # a decoder layer's stacked query/key/value projection weights
+    W_O = 19      # a decoder layer's output projection weights
 
 
 def tensor_id(kind: int, step: int = 0, block: int = 0) -> int:
@@ -107,6 +110,19 @@ def normal_f32(seed: int, tid: int, shape, n0: int = 0, b0: int = 0, h0: int = 0
                         + _sum16(_mix64(base + gold + gold))
                     out[b, h, r:rr] = (s - 393210).astype(np.float32) / np.float32(65536.0)
     return out
+
+
+def draw_view(shape) -> tuple:
+    """The [B, H, N, D] view under which a tensor of another shape (a weight matrix, a
+    [B, S, Dm] activation) draws its values: the leading dims flatten into B, H = 1,
+    and the last dim splits into N x D with D its largest power-of-two divisor up to
+    2**10.  Host and device draws of such a tensor both go through this view."""
+    *lead, last = (int(s) for s in shape)
+    rows = int(np.prod(lead)) if lead else 1
+    c = 1
+    while c < 1024 and last % (2 * c) == 0:
+        c *= 2
+    return (rows, 1, last // c, c)
 
 
 def round_to_bf16_f32(x: np.ndarray) -> np.ndarray:
@@ -180,3 +196,15 @@ def device_fill(t, seed: int, tid: int, rows: int | None = None, n0: int = 0, ro
                                   n0, stream_key(seed, tid), ctypes.c_void_p(stream))
     if rc != 0:
         raise RuntimeError(f"synth_fill_normal failed with HIP error {rc}")
+
+
+def host_draw(seed: int, tid: int, shape, dtype: str):
+    """CPU tensor of any shape, drawn under draw_view(shape)."""
+    return host_tensor(seed, tid, draw_view(shape), dtype).reshape(tuple(int(x) for x in shape))
+
+
+def device_draw(t, seed: int, tid: int) -> None:
+    """Fill the contiguous CUDA tensor ``t`` (any shape) as host_draw would."""
+    if not t.is_contiguous():
+        raise ValueError("device_draw wants a contiguous tensor")
+    device_fill(t.view(draw_view(t.shape)), seed, tid)
