@@ -357,6 +357,83 @@ def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
     )
 
 
+def bench_decoder_layer(steps_per_block, reps, seed):
+    """Attention sublayer of a decoder layer per denoising step (QKV projection, the
+    denoise attention, output projection) at the denoise workload's shape with model
+    width Hq d, over steps_per_block steps with fresh hidden states each."""
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_draw, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, C, S, T = 32, 16, 8, 128, 2048, 32, steps_per_block
+    Dm = Hq * d
+    cap = C + S
+    kc = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    device_fill(kc, seed, tensor_id(K.K_CACHE), rows=C)
+    device_fill(vc, seed, tensor_id(K.V_CACHE), rows=C)
+    xs = []
+    for t in range(T):
+        x = torch.empty((B, S, Dm), dtype=torch.bfloat16, device=dev)
+        device_draw(x, seed, tensor_id(K.X_BLK, step=t))
+        xs.append(x)
+    w_qkv = torch.empty(((Hq + 2 * Hkv) * d, Dm), dtype=torch.bfloat16, device=dev)
+    w_o = torch.empty((Dm, Hq * d), dtype=torch.bfloat16, device=dev)
+    device_draw(w_qkv, seed, tensor_id(K.W_QKV))
+    device_draw(w_o, seed, tensor_id(K.W_O))
+    w_qkv.mul_(2.0 ** -6)  # ~1/sqrt(Dm), a power of two (exact in bf16)
+    w_o.mul_(2.0 ** -6)
+    q = torch.empty((B, Hq, S, d), dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    k = torch.empty((B, Hkv, S, d), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    y = torch.empty((B, S, Dm), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, S), device=dev)
+    nws = m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, Hq, Hkv, S, d, C)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    stream = torch.cuda.current_stream(dev)
+    it = [0]
+
+    def layer_step():
+        m.e2d2_decoder_layer_denoise_step(xs[it[0] % T], w_qkv, w_o, kc, vc, C, q, k, v, o, y,
+                                          lse_blk=lse, workspace=ws)
+        it[0] += 1
+
+    def attn_step():
+        m.e2d2_attn_denoise_step(q, kc, vc, C, k, v, o, lse_blk=lse, workspace=ws)
+
+    x2 = xs[0].view(B * S, Dm)
+    o2 = torch.empty((B * S, Hq * d), dtype=torch.bfloat16, device=dev)
+
+    def lib_gemms():  # the same two products through torch (hipBLASLt), for context
+        torch.matmul(x2, w_qkv.t())
+        torch.matmul(o2, w_o.t())
+
+    res = {}
+    for name, fn in (("layer", layer_step), ("attention", attn_step), ("torch_gemms", lib_gemms)):
+        g = graph_of(fn, T)
+        g.replay()
+        clock_warmup(g.replay)
+        ms = sorted(timed_launches(g.replay, 1, stream)[1] / T for _ in range(reps))
+        res[name] = ms[len(ms) // 2]
+    M = B * S
+    flop = 2 * M * Dm * ((Hq + 2 * Hkv) * d + Hq * d)
+    proj_ms = res["layer"] - res["attention"]
+    return dict(
+        workload="decoder-layer denoise step (QKV projection, attention over cache 2048 + "
+                 "block 32, output projection), B32 Hq16 Hkv8 d128 Dm2048, bf16; "
+                 f"{T} steps with fresh hidden states",
+        us_per_step=round(res["layer"] * 1e3, 2),
+        attention_us=round(res["attention"] * 1e3, 2),
+        projections_us=round(proj_ms * 1e3, 2),
+        projections_tflops=round(flop / (proj_ms * 1e-3) / 1e12, 1),
+        projection_flop_per_step=flop,
+        torch_hipblaslt_gemms_us=round(res["torch_gemms"] * 1e3, 2),
+    )
+
+
 def bench_near_ar(steps, seed):
     """Near-autoregressive decoding: B64 H32 (MHA) d128, a 32768-row cache, block 4.
     Each step streams the whole cache (34 GB), so it is timed eagerly, step by step."""
@@ -445,7 +522,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", choices=["all", "train", "bwd", "layers", "denoise", "long", "nearar",
-                                       "copycal"],
+                                       "declayer", "copycal"],
                     default="all",
                     help="restrict the run (profiling); 'copycal' runs only a plain 1 GiB "
                          "device copy, the reference for scaling HBM byte counters")
@@ -503,6 +580,10 @@ def main():
         print(f"[bench] denoise: warm {out['denoise']['us_per_step_warm']:.1f} us "
               f"({out['denoise']['gbs_warm']:.0f} GB/s), cold {out['denoise']['us_per_step_cold']:.1f} us "
               f"({out['denoise']['gbs_cold']:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    if args.only in ("all", "declayer"):
+        out["decoder_layer"] = bench_decoder_layer(32, 5, 0xE2D20003)
+        print(f"[bench] decoder layer step: {out['decoder_layer']}", file=sys.stderr, flush=True)
 
     if args.only in ("all", "nearar"):
         out["near_ar"] = bench_near_ar(8, 0xE2D20005)

@@ -197,6 +197,39 @@ e2d2_status e2d2_kv_cache_append_varlen(int dtype, int B, int Hkv, int S, int d,
                                         long long max_cache_len, long long cache_cap,
                                         const void* k_new, const void* v_new, void* stream);
 
+/* Attention sublayer of one decoder layer in a denoising step ([Notes] §3 采样算法:
+ * every step of a block calls only the small decoder on the block's S noised tokens;
+ * 方法详解 §2 两种连接方式: with the shared KV cache the decoder layer attends over an
+ * encoder layer's cached clean keys/values plus its own block).  Three launches on
+ * `stream`, in order:
+ *   1. q_blk, k_blk, v_blk = per-head slices of x W_qkv^T;
+ *   2. o_blk, lse_blk = e2d2_attn_denoise_step of q_blk over the cache rows
+ *      [0, cache_len) and the block's own k_blk, v_blk;
+ *   3. y = concat_h(o_blk) W_o^T.
+ * bf16 only (fp32: E2D2_ERR_UNSUPPORTED); d in {32, 64, 128}; fp32 accumulation, every
+ * stored tensor rounded to bf16 (nearest even).  Layouts (all row-major, contiguous):
+ *   x      [B][S][Dm]                hidden states of the block's tokens; Dm % 8 == 0
+ *   w_qkv  [(Hq + 2 Hkv) d][Dm]      rows: query heads 0.., then key heads, then value
+ *                                     heads, d consecutive rows per head (nn.Linear
+ *                                     [out][in] layout)
+ *   w_o    [Dm][Hq d]                column h d + c multiplies o_blk[b][h][s][c]
+ *   k_cache, v_cache, cache_len, cache_cap, lse_blk, workspace: as
+ *                                     e2d2_attn_denoise_step (workspace sized by
+ *                                     e2d2_attn_denoise_workspace_bytes)
+ *   q_blk, o_blk [B][Hq][S][d]; k_blk, v_blk [B][Hkv][S][d]; y [B][S][Dm]: written
+ *                                     (the caller owns them; they must not overlap
+ *                                     each other or the inputs).
+ * Errors: E2D2_ERR_SHAPE also when an operand of the projections reaches 2 GiB;
+ * otherwise as e2d2_attn_denoise_step.  All checks precede the first launch. */
+e2d2_status e2d2_decoder_layer_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                            int Dm, float scale, const void* x,
+                                            const void* w_qkv, const void* w_o,
+                                            const void* k_cache, const void* v_cache,
+                                            long long cache_len, long long cache_cap,
+                                            void* q_blk, void* k_blk, void* v_blk, void* o_blk,
+                                            float* lse_blk, void* y, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
 /* Query/key tile shape (bm query rows of one head, bn keys) the kernels use for a
  * kind, dtype and head dimension.  Host-only; bm and bn are host pointers. */
 e2d2_status e2d2_attn_tile_shape(int kind, int dtype, int d, int* bm, int* bn);

@@ -21,7 +21,9 @@ __all__ = [
     "E2D2Error", "lib", "library_path", "abi_version",
     "e2d2_attn_encoder_blockcausal", "e2d2_attn_train_fwd", "e2d2_attn_denoise_step",
     "e2d2_attn_denoise_workspace_bytes", "e2d2_kv_cache_append", "e2d2_attn_tile_shape",
-    "e2d2_attn_count_tiles", "KIND_ENC", "KIND_DEC", "KIND_DENOISE", "F32", "BF16",
+    "e2d2_attn_count_tiles", "e2d2_attn_denoise_step_varlen", "e2d2_kv_cache_append_varlen",
+    "e2d2_attn_train_bwd", "e2d2_attn_train_bwd_workspace_bytes",
+    "e2d2_decoder_layer_denoise_step", "KIND_ENC", "KIND_DEC", "KIND_DENOISE", "F32", "BF16",
 ]
 
 F32, BF16 = 0, 1
@@ -56,6 +58,9 @@ _SIGS = {
                                          _vp]),
     "e2d2_attn_train_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "e2d2_attn_train_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _f] + [_vp] * 19 + [_sz, _vp]),
+    "e2d2_decoder_layer_denoise_step": (_i, [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp,
+                                             _vp, _ll, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _sz, _vp]),
     "e2d2_attn_tile_shape": (_i, [_i, _i, _i, _int_p, _int_p]),
     "e2d2_attn_count_tiles": (_i, [_i, _i, _i, _i, _i, _ll, _i, _i, _ull_p, _ull_p]),
 }
@@ -319,6 +324,41 @@ def e2d2_kv_cache_append(k_cache, v_cache, cache_len: int, k_new, v_new):
         _dtype_code(k_cache), B, Hkv, S, d, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         int(cache_len), cap, _dev(k_new, "k_new"), _dev(v_new, "v_new"), _stream(k_cache))
     _check("e2d2_kv_cache_append", st)
+
+
+def e2d2_decoder_layer_denoise_step(x, w_qkv, w_o, k_cache, v_cache, cache_len: int, q_blk, k_blk,
+                                    v_blk, o_blk, y, lse_blk=None, workspace=None, scale=None):
+    """Attention sublayer of a decoder layer for one denoising step (bf16): q/k/v =
+    per-head slices of x W_qkv^T, the denoise attention over the cache plus the own
+    block, y = concat_h(o) W_o^T.  x, y [B, S, Dm]; w_qkv [(Hq + 2 Hkv) d, Dm];
+    w_o [Dm, Hq d]; caches [B, Hkv, cap, d]; q_blk, o_blk [B, Hq, S, d] and k_blk,
+    v_blk [B, Hkv, S, d] are written; workspace as e2d2_attn_denoise_step."""
+    B, S, Dm = x.shape
+    _, Hq, _, d = q_blk.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    _same(x.dtype, w_qkv, w_o, k_cache, v_cache, q_blk, k_blk, v_blk, o_blk, y)
+    if tuple(w_qkv.shape) != ((Hq + 2 * Hkv) * d, Dm) or tuple(w_o.shape) != (Dm, Hq * d):
+        raise ValueError("weights must be w_qkv [(Hq + 2 Hkv) d, Dm] and w_o [Dm, Hq d]")
+    if tuple(q_blk.shape) != (B, Hq, S, d) or o_blk.shape != q_blk.shape:
+        raise ValueError("q_blk and o_blk must be [B, Hq, S, d]")
+    if tuple(k_blk.shape) != (B, Hkv, S, d) or v_blk.shape != k_blk.shape:
+        raise ValueError("k_blk and v_blk must be [B, Hkv, S, d]")
+    if tuple(k_cache.shape) != (B, Hkv, cap, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, cap, d]")
+    if y.shape != x.shape:
+        raise ValueError("y must be [B, S, Dm]")
+    if lse_blk is not None and (lse_blk.dtype != torch.float32 or tuple(lse_blk.shape) != (B, Hq, S)):
+        raise ValueError("lse must be float32 [B, Hq, S]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace", workspace.dim()), workspace.numel() * workspace.element_size()
+    st = lib().e2d2_decoder_layer_denoise_step(
+        _dtype_code(x), B, Hq, Hkv, S, d, Dm, _default_scale(d, scale), _dev(x, "x", 3),
+        _dev(w_qkv, "w_qkv", 2), _dev(w_o, "w_o", 2), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), int(cache_len), cap, _dev(q_blk, "q_blk"), _dev(k_blk, "k_blk"),
+        _dev(v_blk, "v_blk"), _dev(o_blk, "o_blk"), _opt(lse_blk, "lse_blk", 3), _dev(y, "y", 3),
+        ws_ptr, ws_bytes, _stream(x))
+    _check("e2d2_decoder_layer_denoise_step", st)
 
 
 def e2d2_attn_tile_shape(kind: int, dtype: int, d: int):

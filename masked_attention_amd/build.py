@@ -27,7 +27,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 
-SOURCES = ["api.hip", "attn_train.hip", "attn_denoise.hip", "attn_bwd.hip"]
+SOURCES = ["api.hip", "attn_train.hip", "attn_denoise.hip", "attn_bwd.hip", "linear.hip"]
 
 
 def _run(cmd):

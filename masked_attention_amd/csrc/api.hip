@@ -297,7 +297,8 @@ e2d2_status denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float 
                          const int* lens, long long cache_len, long long cache_cap,
                          const void* k_blk, const void* v_blk, void* o_blk, float* lse_blk,
                          void* workspace, size_t workspace_bytes,
-                         unsigned long long* dbg_tile_visits, void* stream) {
+                         unsigned long long* dbg_tile_visits, void* stream,
+                         bool launch = true) {
   if (dtype != E2D2_F32 && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
   if (lens != nullptr && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
   if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
@@ -315,13 +316,19 @@ e2d2_status denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float 
   const size_t need = denoise_ws_bytes(dtype, B, Hq, Hkv, S, d, cache_len);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return E2D2_ERR_WORKSPACE;
+  if (dtype == E2D2_BF16) {
+    const DenoiseShape sh = denoise_shape(B, Hq, Hkv, S, cache_len);
+    if ((long long)B * Hkv * sh.n_qgroups * sh.n_split > INT32_MAX) return E2D2_ERR_SHAPE;
+  } else if ((long long)B * Hq * cdiv(S, e2d2::kF32TileBM) > INT32_MAX) {
+    return E2D2_ERR_SHAPE;
+  }
+  if (!launch) return E2D2_OK;
   hipStream_t s = (hipStream_t)stream;
   // An empty cache has no rows to read; any non-NULL pointer stands in.
   const void* kc = cache_len > 0 ? k_cache : k_blk;
   const void* vc = cache_len > 0 ? v_cache : v_blk;
   if (dtype == E2D2_BF16) {
     const DenoiseShape sh = denoise_shape(B, Hq, Hkv, S, cache_len);
-    if ((long long)B * Hkv * sh.n_qgroups * sh.n_split > INT32_MAX) return E2D2_ERR_SHAPE;
     e2d2::DenoiseParams p = {};
     p.q = (const __bf16*)q_blk;
     p.k_cache = (const __bf16*)kc;
@@ -367,7 +374,6 @@ e2d2_status denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float 
   p.kinds[0] = p.kinds[1] = e2d2::kDenoise;
   p.n_kinds = 1;
   p.n_qtiles = cdiv(S, e2d2::kF32TileBM);
-  if ((long long)B * Hq * p.n_qtiles > INT32_MAX) return E2D2_ERR_SHAPE;
   return hip_status(e2d2::launch_attn_f32(p, d, s));
 }
 
@@ -397,6 +403,90 @@ e2d2_status e2d2_attn_denoise_step_varlen(int dtype, int B, int Hq, int Hkv, int
   return denoise_step(dtype, B, Hq, Hkv, S, d, scale, q_blk, k_cache, v_cache, cache_lens,
                       max_cache_len, cache_cap, k_blk, v_blk, o_blk, lse_blk, workspace,
                       workspace_bytes, dbg_tile_visits, stream);
+}
+
+e2d2_status e2d2_decoder_layer_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                            int Dm, float scale, const void* x,
+                                            const void* w_qkv, const void* w_o,
+                                            const void* k_cache, const void* v_cache,
+                                            long long cache_len, long long cache_cap,
+                                            void* q_blk, void* k_blk, void* v_blk, void* o_blk,
+                                            float* lse_blk, void* y, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (dtype != E2D2_BF16 || !head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Dm <= 0 || Hq % Hkv != 0 || Dm % 8 != 0)
+    return E2D2_ERR_SHAPE;
+  if (!x || !w_qkv || !w_o || !y) return E2D2_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(w_o) || !aligned16(y))
+    return E2D2_ERR_SHAPE;
+  // Every operand of the projections is addressed with 32-bit byte offsets.
+  const long long M = (long long)B * S;
+  const long long n_qkv = (long long)(Hq + 2 * Hkv) * d;
+  const long long k_o = (long long)Hq * d;
+  const long long lim = 1ll << 31;
+  if (M * Dm * 2 >= lim || n_qkv * Dm * 2 >= lim || Dm * k_o * 2 >= lim || M * k_o * 2 >= lim)
+    return E2D2_ERR_SHAPE;
+  // the attention's own checks (pointers, cache, workspace), before anything launches
+  e2d2_status st = denoise_step(dtype, B, Hq, Hkv, S, d, scale, q_blk, k_cache, v_cache, nullptr,
+                                cache_len, cache_cap, k_blk, v_blk, o_blk, lse_blk, workspace,
+                                workspace_bytes, nullptr, stream, false);
+  if (st != E2D2_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int log2d = 0;
+  while ((1 << log2d) < d) ++log2d;
+
+  // q, k, v = x W_qkv^T, written per head
+  e2d2::LinearParams lp = {};
+  lp.a = (const __bf16*)x;
+  lp.w = (const __bf16*)w_qkv;
+  lp.c[0] = (__bf16*)q_blk;
+  lp.c[1] = (__bf16*)k_blk;
+  lp.c[2] = (__bf16*)v_blk;
+  lp.c_n0[0] = 0;
+  lp.c_n0[1] = Hq * d;
+  lp.c_n0[2] = (Hq + Hkv) * d;
+  lp.c_h[0] = Hq;
+  lp.c_h[1] = lp.c_h[2] = Hkv;
+  lp.c_w = d;
+  lp.a_sb = S * Dm;
+  lp.a_ss = Dm;
+  lp.a_sh = 0;
+  lp.a_heads = 0;
+  lp.M = (int)M;
+  lp.N = (int)n_qkv;
+  lp.K = Dm;
+  lp.S = S;
+  lp.a_bytes = (unsigned)(M * Dm * 2);
+  lp.w_bytes = (unsigned)(n_qkv * Dm * 2);
+  hipError_t e = e2d2::launch_linear_bf16(lp, s);
+  if (e != hipSuccess) return hip_status(e);
+
+  st = denoise_step(dtype, B, Hq, Hkv, S, d, scale, q_blk, k_cache, v_cache, nullptr, cache_len,
+                    cache_cap, k_blk, v_blk, o_blk, lse_blk, workspace, workspace_bytes, nullptr,
+                    stream);
+  if (st != E2D2_OK) return st;
+
+  // y = concat_h(o) W_o^T, o read per head
+  e2d2::LinearParams op = {};
+  op.a = (const __bf16*)o_blk;
+  op.w = (const __bf16*)w_o;
+  op.c[0] = op.c[1] = op.c[2] = (__bf16*)y;
+  op.c_n0[0] = 0;
+  op.c_n0[1] = op.c_n0[2] = Dm;
+  op.c_h[0] = op.c_h[1] = op.c_h[2] = 1;
+  op.c_w = Dm;
+  op.a_sb = Hq * S * d;
+  op.a_ss = d;
+  op.a_sh = S * d;
+  op.a_heads = 1;
+  op.a_log2w = log2d;
+  op.M = (int)M;
+  op.N = Dm;
+  op.K = (int)k_o;
+  op.S = S;
+  op.a_bytes = (unsigned)(M * k_o * 2);
+  op.w_bytes = (unsigned)(Dm * k_o * 2);
+  return hip_status(e2d2::launch_linear_bf16(op, s));
 }
 
 e2d2_status e2d2_kv_cache_append_varlen(int dtype, int B, int Hkv, int S, int d, void* k_cache,

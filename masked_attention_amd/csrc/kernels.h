@@ -93,6 +93,27 @@ struct BwdParams {
   float c;       // scale * log2(e)
 };
 
+// C = A W^T for the projections of a decoder layer, bf16 in and out, fp32 accumulate.
+// Row m < M = B*S is (b, s) = (m / S, m % S).  A(m, k) is element
+//   (b a_sb + s a_ss) + (a_heads ? (k >> a_log2w) a_sh + (k & (2^a_log2w - 1)) : k)
+// of a; W is [N][K].  Column n belongs to segment seg (c_n0[seg] <= n < c_n0[seg+1],
+// c_n0[0] = 0, unused boundaries = N); with nn = n - c_n0[seg], h = nn / c_w and
+// c = nn % c_w, C(m, n) goes to c[seg][((b c_h[seg] + h) S + s) c_w + c].
+// a_bytes, w_bytes: sizes of the A and W buffers (reads past them return zero).
+struct LinearParams {
+  const __bf16* a;
+  const __bf16* w;
+  __bf16* c[3];
+  int c_n0[3];
+  int c_h[3];
+  int c_w;
+  int a_sb, a_ss, a_sh;
+  int a_heads, a_log2w;
+  int M, N, K, S;
+  unsigned a_bytes, w_bytes;
+};
+hipError_t launch_linear_bf16(const LinearParams& p, hipStream_t stream);
+
 int train_tile_bm(int d);
 int bwd_tile_rows();
 hipError_t launch_train_bwd_bf16(const BwdParams& p, int d, hipStream_t stream);

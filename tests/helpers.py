@@ -17,9 +17,9 @@ F32_RTOL = 1e-5
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-def host(shape, seed, kind, dtype, step=0, block=0, n0=0):
-    """CPU tensor from the seeded generator."""
-    return host_tensor(seed, tensor_id(kind, step, block), shape, dtype, n0=n0)
+def host(shape, seed, kind, dtype, step=0, block=0, n0=0, b0=0):
+    """CPU tensor from the seeded generator (rows from n0, batches from b0)."""
+    return host_tensor(seed, tensor_id(kind, step, block), shape, dtype, n0=n0, b0=b0)
 
 
 def on_gpu(shape, seed, kind, dtype, step=0, block=0):

@@ -207,3 +207,29 @@ def test_train_bwd_validation_returns_before_launch():
     assert m.e2d2_attn_train_bwd_workspace_bytes(m.BF16, 1, 2, 64, False) * 2 == need
     assert _bwd(q_enc=16, o_enc=16, lse_enc=16, do_enc=16, dq_enc=16, ws_bytes=need - 1) == ERR_WORKSPACE
     assert m.e2d2_attn_train_bwd_workspace_bytes(m.F32, 1, 2, 64, True) == 0
+
+
+def _layer(**kw):
+    a = dict(dtype=m.BF16, B=2, Hq=4, Hkv=2, S=8, d=64, Dm=256, scale=0.125, x=16, w_qkv=16,
+             w_o=16, k_cache=16, v_cache=16, cache_len=100, cache_cap=128, q_blk=16, k_blk=16,
+             v_blk=16, o_blk=16, lse_blk=None, y=16, ws=16, ws_bytes=1 << 24, stream=None)
+    a.update(kw)
+    return m.lib().e2d2_decoder_layer_denoise_step(*a.values())
+
+
+def test_layer_validation_returns_before_launch():
+    assert _layer(x=None) == ERR_NULL
+    assert _layer(w_o=None) == ERR_NULL
+    assert _layer(y=None) == ERR_NULL
+    assert _layer(q_blk=None) == ERR_NULL             # the attention's own checks run first too
+    assert _layer(k_cache=None) == ERR_NULL
+    assert _layer(dtype=m.F32) == ERR_UNSUPPORTED
+    assert _layer(d=48) == ERR_UNSUPPORTED
+    assert _layer(Dm=100) == ERR_SHAPE                # rows of x must be whole 16-byte chunks
+    assert _layer(Hq=3) == ERR_SHAPE
+    assert _layer(x=24) == ERR_SHAPE                  # misaligned
+    assert _layer(cache_len=200) == ERR_SHAPE         # past the capacity
+    assert _layer(B=1 << 14, S=1 << 10, Dm=1 << 10) == ERR_SHAPE  # x reaches 2 GiB
+    need = m.e2d2_attn_denoise_workspace_bytes(m.BF16, 1, 2, 1, 8, 128, 1 << 16)
+    assert need > 0
+    assert _layer(B=1, Hq=2, Hkv=1, d=128, cache_len=1 << 16, cache_cap=1 << 16, ws=None) == ERR_WORKSPACE
