@@ -46,6 +46,10 @@ constexpr int kWaves = kPairs * kNQB;  // wave = 2 * pair + column block
 constexpr int kThreads = kWaves * 64;
 constexpr float kBound = 65536.f;      // lane sum of a block's numerators forcing a rescale
 constexpr float kNegBig = -1e30f;      // "no key yet" running max
+// Row pitch (floats) of the partial O rows merged in LDS: padded by 4 so that the 32
+// rows one wave writes (one per lane) spread over the banks instead of sharing one.
+template <int D>
+constexpr int kOPitch = D + 4;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p) {
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p)
     for (int v = 0; v < kPairs; ++v) M = fmaxf(M, mw[(v * kNQB + qi) * 32 + row]);
     const float mine = mw[(pair * kNQB + qi) * 32 + row];
     const float f = mine == -INFINITY ? 0.f : fast_exp2(mine - M);
-    float* dst = ow + ((size_t)pair * kNQB * 32 + qi * 32 + row) * D;
+    float* dst = ow + ((size_t)pair * kNQB * 32 + qi * 32 + row) * kOPitch<D>;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void denoise_bf16_kernel(DenoiseParams p)
       const float mv = mw[(v * kNQB + cq) * 32 + rr];
       const float f = mv == -INFINITY ? 0.f : fast_exp2(mv - M);
       lt += (lw[(v * kNQB + cq) * 64 + rr] + lw[(v * kNQB + cq) * 64 + rr + 32]) * f;
-      const f32x4 x = *(const f32x4*)(ow + ((size_t)v * kNQB * 32 + r) * D + d);
+      const f32x4 x = *(const f32x4*)(ow + ((size_t)v * kNQB * 32 + r) * kOPitch<D> + d);
       acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
     }
     if (p.n_split == 1) {
@@ -324,7 +328,7 @@ template <int D>
 size_t denoise_smem() {
   const size_t stream = (size_t)kPairs * 2 * 2 * kTN * D * sizeof(__bf16);
   const size_t merge = (size_t)kPairs * kNQB * (32 + 64) * sizeof(float) +
-                       (size_t)kPairs * kNQB * 32 * D * sizeof(float);
+                       (size_t)kPairs * kNQB * 32 * kOPitch<D> * sizeof(float);
   return stream > merge ? stream : merge;
 }
 
