@@ -594,6 +594,8 @@ def main():
         print(json.dumps(out))
         return
     value = train["useful_flop"] / (train["ms_per_step"] * 1e-3) / 1e12
+    tB, tH, tL, td = 8, 16, 1024, 64
+    alg_bytes = 6 * tB * tH * tL * td * 2 + 2 * tB * tH * tL * td * 2 + 2 * tB * tH * tL * 4
     achieved = train["useful_flop"] / (train["kernel_ms"] * 1e-3) / 1e12
     traffic = None
     try:
@@ -624,7 +626,11 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "train_fwd_bf16_kernel<64>",
                      "kernel_us": round(train["kernel_ms"] * 1e3, 2),
-                     "useful_flop_per_launch": train["useful_flop"]},
+                     "useful_flop_per_launch": train["useful_flop"],
+                     # six bf16 inputs in, two outputs and two LSE arrays out, each once
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "flop_per_byte": round(train["useful_flop"] / alg_bytes, 1),
+                     "hbm_roof_tflops": round(train["useful_flop"] / alg_bytes * PEAK_HBM_GBS / 1e3, 1)},
     }
     line.update(out)
     if not args.no_cpu_baseline:
