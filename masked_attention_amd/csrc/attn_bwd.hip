@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
     qt = (ss ? qs.qt01 : qs.qt00) + w % nq;
   };
 
-  TileLoader<D, kTK, kWaves> loader;
+  TileDma<D, kTK, kWaves> loader;
   loader.init(wave, lane);
   char E2D2_LDS* lds_b = (char E2D2_LDS*)smem_raw;
   const uint32_t q_bytes = (uint32_t)L * D * 2u;
@@ -338,15 +338,14 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
     const int sl = ss ? qs.slot1 : qs.slot0;
     char E2D2_LDS* st = lds_b + (u & 1) * STAGE_B;
     const size_t row_base = ((size_t)b * p.Hq + hq) * (size_t)L;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((sl ? p.q[1] : p.q[0]) + row_base * D, q_bytes);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc((sl ? p.dO[1] : p.dO[0]) + row_base * D, q_bytes);
+    const BufDesc rq = buf_desc((sl ? p.q[1] : p.q[0]) + row_base * D, q_bytes);
+    const BufDesc rd = buf_desc((sl ? p.dO[1] : p.dO[0]) + row_base * D, q_bytes);
     loader.load(rq, qt * kTK, st, wave);
     loader.load(rd, qt * kTK, st + TILE * 2, wave);
     if (wave < 2) {  // the 64 rows' lse2 (wave 0) and delta (wave 1), 4 bytes per lane
       const float* src_f = wave == 0 ? (sl ? p.lse2[1] : p.lse2[0]) : (sl ? p.delta[1] : p.delta[0]);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src_f + row_base, (uint32_t)L * 4u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void E2D2_LDS*)(st + 2 * TILE * 2 + wave * 256), 4,
-                                               lane * 4, qt * kTK * 4, 0, 0);
+      dma_lds4(buf_desc(src_f + row_base, (uint32_t)L * 4u), (uint32_t)(lane * 4),
+               (uint32_t)(qt * kTK * 4), lds_addr(st + 2 * TILE * 2 + wave * 256));
     }
   };
   if (ntot > 0) issue(0);
@@ -383,7 +382,6 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
   k_offsets<D>(lane, koff);
   uint32_t offA[NDB], offB[NDB];
   vt_offsets<D>(lane, offA, offB);
-  const uint32_t lds0 = lds_addr(lds_b);
   const float c = p.c;
 
   f32x16 dk[NDB], dv[NDB];
@@ -394,25 +392,16 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
   }
 
   // rows of a 32-row block (KB) of the tile at LDS offset BASE, times the registers w:
-  // the S = Q K^T (or dP = dO V^T) block; operands read half at a time (registers)
+  // the S = Q K^T (or dP = dO V^T) block.  The LDS reads of this kernel are left to
+  // the compiler (its loads are issued from asm, see TileDma), which overlaps them
+  // with the MFMAs: at one or two waves per SIMD nothing else hides their latency.
+  const char E2D2_LDS* ldsc = (const char E2D2_LDS*)smem_raw;
   auto rows_dot = [&](auto kbc, auto basec, const bf16x8 (&w)[NC]) __attribute__((always_inline)) {
     constexpr int KB = decltype(kbc)::value, BASE = decltype(basec)::value;
+    constexpr int OFF = BASE + KB * 64 * D;
     f32x16 acc = zero16();
-    if constexpr (NC >= 4) {
-      constexpr int H = NC / 2;
-      bf16x8 a[H];
-      kread_part<D, KB, BASE, 0, H>(lds0, koff, a);
 #pragma unroll
-      for (int cc = 0; cc < H; ++cc) acc = mfma32(a[cc], w[cc], acc);
-      kread_part<D, KB, BASE, H, H>(lds0, koff, a);
-#pragma unroll
-      for (int cc = 0; cc < H; ++cc) acc = mfma32(a[cc], w[H + cc], acc);
-    } else {
-      bf16x8 a[NC];
-      kread_block<D, KB, BASE>(lds0, koff, a);
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) acc = mfma32(a[cc], w[cc], acc);
-    }
+    for (int cc = 0; cc < NC; ++cc) acc = mfma32(lds_read16<OFF>(ldsc, koff[cc]), w[cc], acc);
     return acc;
   };
   // query block qb (32 rows) of the tile in stage STG, stream slot ss, query tile qt
@@ -456,12 +445,12 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
       const bf16x8 pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       const bf16x8 dsb = to_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
       bf16x8 tf[NDB];
-      if (h == 0) read_vt_half32<D, DOFF + QB * 64 * D, 0>(lds0, offA, offB, tf);
-      else read_vt_half32<D, DOFF + QB * 64 * D, 1>(lds0, offA, offB, tf);
+      if (h == 0) read_vt_half32_lds<D, DOFF + QB * 64 * D, 0>(ldsc, offA, offB, tf);
+      else read_vt_half32_lds<D, DOFF + QB * 64 * D, 1>(ldsc, offA, offB, tf);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dv[db] = mfma32(tf[db], pb, dv[db]);
-      if (h == 0) read_vt_half32<D, QOFF + QB * 64 * D, 0>(lds0, offA, offB, tf);
-      else read_vt_half32<D, QOFF + QB * 64 * D, 1>(lds0, offA, offB, tf);
+      if (h == 0) read_vt_half32_lds<D, QOFF + QB * 64 * D, 0>(ldsc, offA, offB, tf);
+      else read_vt_half32_lds<D, QOFF + QB * 64 * D, 1>(ldsc, offA, offB, tf);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dk[db] = mfma32(tf[db], dsb, dk[db]);
     }

@@ -577,4 +577,82 @@ __device__ __forceinline__ uint32_t lds_addr(const void E2D2_LDS* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
+
+// ---------------------------------------------------------------------------------
+// Direct-to-LDS loads issued from inline asm, and LDS operand reads left to the
+// compiler.  With the builtin buffer_load ... lds the compiler sees an LDS write in
+// flight and waits for every outstanding load (s_waitcnt vmcnt(0)) before any LDS read
+// it can see, which serialises the prefetch.  Issued from asm (no output registers: the
+// loads write LDS only), the loads are invisible to it; the caller waits for the stage
+// it reads with wait_vmem and crosses a barrier.  The reads are then plain LDS loads
+// (or the ds_read_b64_tr_b16 builtin) that the compiler schedules against the MFMAs
+// with partial lgkmcnt waits.
+
+// Raw buffer descriptor words (base, byte size; reads past the size return zero).
+typedef int BufDesc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ BufDesc buf_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  BufDesc r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+// 16 (dma_lds16) or 4 (dma_lds4) bytes per lane from buffer offset voff + soff into
+// LDS at lds + 16 * lane (4 * lane); lds and soff wave-uniform.
+__device__ __forceinline__ void dma_lds16(BufDesc d, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(d), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(BufDesc d, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(d), "s"(soff), "s"(lds) : "memory", "m0");
+}
+// TileLoader's layout and work split, loads issued with dma_lds16.
+template <int D, int ROWS, int NWAVES>
+struct TileDma {
+  static constexpr int CH = D / 8;
+  static constexpr int NI = ROWS * CH / 64;
+  static constexpr int NPW = NI / NWAVES;
+  static_assert(NI % NWAVES == 0 && ROWS * CH % 64 == 0, "tile does not split evenly");
+  uint32_t voff[NPW];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < NPW; ++k) {
+      const int slot = (wave + k * NWAVES) * 64 + lane;
+      const int r = slot / CH;
+      const int lc = (slot % CH) ^ swz<D>(r);
+      voff[k] = (uint32_t)(r * D + lc * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void load(BufDesc d, int row0, char E2D2_LDS* tile, int wave) const {
+#pragma unroll
+    for (int k = 0; k < NPW; ++k)
+      dma_lds16(d, voff[k], (uint32_t)(row0 * D * 2), lds_addr(tile + (wave + k * NWAVES) * 1024));
+  }
+};
+// 16 bytes at base + off + OFF (compiler-scheduled).
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read16(const char E2D2_LDS* base, uint32_t off) {
+  return *(const bf16x8 E2D2_LDS*)(base + off + OFF);
+}
+// ds_read_b64_tr_b16 at base + off + OFF (compiler-scheduled).
+template <int OFF>
+__device__ __forceinline__ long lds_read_tr(const char E2D2_LDS* base, uint32_t off) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 E2D2_LDS*)(base + off + OFF));
+  return __builtin_bit_cast(long, v);
+}
+// read_vt_half32 with compiler-scheduled reads.
+template <int D, int BASE, int H>
+__device__ __forceinline__ void read_vt_half32_lds(const char E2D2_LDS* base,
+                                                   const uint32_t (&offA)[D / 32],
+                                                   const uint32_t (&offB)[D / 32],
+                                                   bf16x8 (&vf)[D / 32]) {
+  constexpr int O = BASE + H * 32 * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+    vf[db] = join_bf16(lds_read_tr<O>(base, offA[db]), lds_read_tr<O>(base, offB[db]));
+}
+
 }  // namespace e2d2

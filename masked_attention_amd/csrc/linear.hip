@@ -55,28 +55,6 @@ struct LinGeo {
   static constexpr int LDS = ST * STAGE > C_BYTES ? ST * STAGE : C_BYTES;
 };
 
-// Raw buffer descriptor (base, byte size; loads past the end return zero) as four
-// dwords for inline asm.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);
-  r[2] = (int)bytes;
-  r[3] = 0x00020000;
-  return r;
-}
-
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.  Written as
-// inline asm so that the compiler does not see an LDS write in flight and wait for
-// every outstanding load before each LDS read; the caller waits (wait_vmem) for the
-// stage it reads and passes a barrier.  No output registers.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
-}
-
 // Wait until at most n (0 <= n < 4, run time) groups of G loads of this wave remain.
 template <int G>
 __device__ __forceinline__ void wait_groups(int n) {
@@ -101,8 +79,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void linear_bf16_kernel(
   const int m0 = (blockIdx.x / n_tiles_n) * G::MT;
   const int nk = (p.K + kKS - 1) / kKS;
 
-  const i32x4 rw = rsrc_words(p.w, p.w_bytes);
-  const i32x4 ra = rsrc_words(p.a, p.a_bytes);
+  const BufDesc rw = buf_desc(p.w, p.w_bytes);
+  const BufDesc ra = buf_desc(p.a, p.a_bytes);
 
   // Per-lane load slots.  Load i of this lane fills LDS slot (wave + WAVES i) * 64 +
   // lane of the W (or A) part of a stage: row r = slot / 8, physical chunk slot % 8,
@@ -143,7 +121,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void linear_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < NLW; ++i) {
       const uint32_t off = w_col[i] < kv ? w_base[i] + (uint32_t)(k0 * 2) : kOOB;
-      dma16(rw, off, lds_addr(st + (wave + i * WAVES) * 1024));
+      dma_lds16(rw, off, 0, lds_addr(st + (wave + i * WAVES) * 1024));
     }
 #pragma unroll
     for (int i = 0; i < NLA; ++i) {
@@ -153,7 +131,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void linear_bf16_kernel(
         const int kk = p.a_heads ? ((k >> p.a_log2w) * p.a_sh + (k & ((1 << p.a_log2w) - 1))) : k;
         off = a_row[i] + (uint32_t)(kk * 2);
       }
-      dma16(ra, off, lds_addr(st + G::W_BYTES + (wave + i * WAVES) * 1024));
+      dma_lds16(ra, off, 0, lds_addr(st + G::W_BYTES + (wave + i * WAVES) * 1024));
     }
   };
 
@@ -175,7 +153,6 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void linear_bf16_kernel(
   if (ST > 2 && 1 < nk) issue(1, IntC<1>{});
   if (ST > 3 && 2 < nk) issue(2, IntC<2 % ST>{});
   auto step = [&](int kt, auto stg) __attribute__((always_inline)) {
-    constexpr int OFF = decltype(stg)::value * STAGE;
     // stage kt landed; the stages issued after it (up to ST - 2) may still be in flight
     wait_groups<NL>(min(ST - 2, nk - 1 - kt));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
