@@ -89,7 +89,7 @@ def check_rel(got, ref, what, rel=2e-2):
     (3, 32, 256, 4, 2, 64, 300),   # several k stages, grouped heads
     (2, 16, 512, 4, 4, 128, 0),    # empty cache: the own block only
     (1, 1, 64, 2, 1, 64, 33),      # one token
-    (4, 32, 1024, 8, 4, 128, 700), # tiles of 128 x 128 (enough for one per CU is not needed)
+    (4, 32, 1024, 8, 4, 128, 700), # 16 k stages, a 128-row token tile, two heads per kv head
 ])
 def test_layer_matches_oracle(B, S, Dm, Hq, Hkv, d, C):
     seed = 0xE2D2C300 + Dm + C
@@ -164,3 +164,47 @@ def test_layer_is_deterministic_and_matches_device_inputs():
     b = _run(x, w_qkv, w_o, kc, vc, C, Hq, Hkv, d)
     for name, u, w in zip(["q", "k", "v", "o", "lse", "y"], a, b):
         assert torch.equal(u, w), name
+
+
+def test_layer_graph_replays_follow_new_hidden_states():
+    # One captured layer step replayed while the hidden states change on the device (a
+    # denoising loop feeds each step's tokens back in): every replay equals an eager call.
+    B, S, Dm, Hq, Hkv, d, C = 2, 16, 256, 4, 2, 64, 150
+    seed = 0xE2D2C700
+    xh, w_qkv, w_o = _host_inputs(B, S, Dm, Hq, Hkv, d, seed)
+    x, w_qkv, w_o = xh.cuda(), w_qkv.cuda(), w_o.cuda()
+    kc = gpu_fill((B, Hkv, C, d), seed, K.K_CACHE, "bf16")
+    vc = gpu_fill((B, Hkv, C, d), seed, K.V_CACHE, "bf16")
+    q = torch.empty((B, Hq, S, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    k = torch.empty((B, Hkv, S, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    y = torch.empty_like(x)
+    n = m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, Hq, Hkv, S, d, C)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+
+    def step(out):
+        m.e2d2_decoder_layer_denoise_step(x, w_qkv, w_o, kc, vc, C, q, k, v, o, out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(y)
+    ref = torch.empty_like(y)
+    for it in range(3):
+        x.mul_(-0.5).add_(0.25)  # eager update between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        step(ref)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {it}"
+    xf = x.cpu()
+    want = oracle.decoder_layer_denoise(xf, w_qkv.cpu(), w_o.cpu(), kc.cpu(), vc.cpu(), C, Hq, Hkv,
+                                        d, scale_of(d))
+    check_rel(y, want[5], "y after replays")
