@@ -374,3 +374,8 @@ def e2d2_attn_count_tiles(kind: int, B: int, Hq: int, L: int, S: int, cache_len:
     _check("e2d2_attn_count_tiles", lib().e2d2_attn_count_tiles(
         kind, B, Hq, L, S, int(cache_len), bm, bn, ctypes.byref(v), ctypes.byref(f)))
     return v.value, f.value
+
+
+from .autograd import e2d2_attention  # noqa: E402  (needs the wrappers above)
+
+__all__.append("e2d2_attention")
