@@ -350,50 +350,47 @@ hipError_t launch_denoise_d(const DenoiseParams& p, hipStream_t stream) {
 }
 
 // Bitwise copy of the new block's K and V rows into the caches, 16 bytes per lane.
-__global__ __launch_bounds__(256) void kv_append_kernel(int row_bytes, int S, int BH,
-                                                        char* k_cache, char* v_cache,
-                                                        long long cache_len, long long cap,
-                                                        const char* k_new, const char* v_new) {
-  const int per_row = row_bytes / 16;
-  const long long per_tensor = (long long)BH * S * per_row;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * per_tensor;
-       i += (long long)gridDim.x * blockDim.x) {
-    const bool is_v = i >= per_tensor;
-    const long long j = is_v ? i - per_tensor : i;
-    const int ch = (int)(j % per_row);
-    const long long rs = j / per_row;  // (bh, s)
-    const int s = (int)(rs % S);
-    const long long bh = rs / S;
-    const char* src = (is_v ? v_new : k_new) + (rs * per_row + ch) * 16;
-    char* dst = (is_v ? v_cache : k_cache) + ((bh * cap + cache_len + s) * per_row + ch) * 16;
-    *(int4*)dst = *(const int4*)src;
+// Workgroup = (sequence-head bh, 256 16-byte chunks of its S rows); row s of bh goes to
+// cache row len + s, with len = cache_len, or lens[b] when lens is given (a sequence
+// whose length is outside [0, max_len] is left untouched).  Chunks per row are a power
+// of two, so the index arithmetic is shifts and masks.
+__global__ __launch_bounds__(256) void kv_append_kernel(int per_row_log2, int S, int Hkv,
+                                                        int blocks_per_bh, int4* k_cache,
+                                                        int4* v_cache, long long cache_len,
+                                                        long long max_len, long long cap,
+                                                        const int4* k_new, const int4* v_new,
+                                                        const int* lens) {
+  const int bh = blockIdx.x / blocks_per_bh;  // uniform
+  const int j = (blockIdx.x - bh * blocks_per_bh) * 256 + threadIdx.x;
+  if (j >= (S << per_row_log2)) return;
+  long long len = cache_len;
+  if (lens != nullptr) {
+    len = lens[bh / Hkv];
+    if (len < 0 || len > max_len) return;
   }
+  const int s = j >> per_row_log2;
+  const int ch = j & ((1 << per_row_log2) - 1);
+  const size_t src = (((size_t)bh * S + s) << per_row_log2) + ch;
+  const size_t dst = (((size_t)bh * cap + len + s) << per_row_log2) + ch;
+  k_cache[dst] = k_new[src];
+  v_cache[dst] = v_new[src];
 }
 
-// Per-sequence append: like kv_append_kernel, with sequence b's rows written at
-// lens[b] (skipped when lens[b] is outside [0, max_len]; the host checked that
-// max_len + S fits the capacity).
-__global__ __launch_bounds__(256) void kv_append_varlen_kernel(int row_bytes, int S, int Hkv, int BH,
-                                                               char* k_cache, char* v_cache,
-                                                               const int* lens, long long max_len,
-                                                               long long cap, const char* k_new,
-                                                               const char* v_new) {
-  const int per_row = row_bytes / 16;
-  const long long per_tensor = (long long)BH * S * per_row;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * per_tensor;
-       i += (long long)gridDim.x * blockDim.x) {
-    const bool is_v = i >= per_tensor;
-    const long long j = is_v ? i - per_tensor : i;
-    const int ch = (int)(j % per_row);
-    const long long rs = j / per_row;  // (bh, s)
-    const int s = (int)(rs % S);
-    const long long bh = rs / S;
-    const long long len = lens[bh / Hkv];
-    if (len < 0 || len > max_len) continue;
-    const char* src = (is_v ? v_new : k_new) + (rs * per_row + ch) * 16;
-    char* dst = (is_v ? v_cache : k_cache) + ((bh * cap + len + s) * per_row + ch) * 16;
-    *(int4*)dst = *(const int4*)src;
-  }
+hipError_t launch_append(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
+                         void* v_cache, long long cache_len, const int* lens, long long max_len,
+                         long long cap, const void* k_new, const void* v_new, hipStream_t stream) {
+  const int per_row = d * elem_bytes / 16;
+  int log2 = 0;
+  while ((1 << log2) < per_row) ++log2;
+  if ((1 << log2) != per_row) return hipErrorInvalidValue;
+  const long long bh = (long long)B * Hkv;
+  const long long bpb = (((long long)S << log2) + 255) / 256;
+  if (bh * bpb == 0) return hipSuccess;
+  if (bh * bpb > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)(bh * bpb)), dim3(256), 0, stream, log2, S,
+                     Hkv, (int)bpb, (int4*)k_cache, (int4*)v_cache, cache_len, max_len, cap,
+                     (const int4*)k_new, (const int4*)v_new, lens);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -421,29 +418,15 @@ hipError_t launch_denoise_bf16(const DenoiseParams& p, int d, hipStream_t stream
 hipError_t launch_kv_append(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
                             void* v_cache, long long cache_len, long long cap, const void* k_new,
                             const void* v_new, hipStream_t stream) {
-  const int row_bytes = d * elem_bytes;
-  const long long total = 2ll * B * Hkv * S * (row_bytes / 16);
-  if (total == 0) return hipSuccess;
-  long long blocks = (total + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, row_bytes, S,
-                     B * Hkv, (char*)k_cache, (char*)v_cache, cache_len, cap,
-                     (const char*)k_new, (const char*)v_new);
-  return hipGetLastError();
+  return launch_append(elem_bytes, B, Hkv, S, d, k_cache, v_cache, cache_len, nullptr, cache_len,
+                       cap, k_new, v_new, stream);
 }
 
 hipError_t launch_kv_append_varlen(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
                                    void* v_cache, const int* lens, long long max_len, long long cap,
                                    const void* k_new, const void* v_new, hipStream_t stream) {
-  const int row_bytes = d * elem_bytes;
-  const long long total = 2ll * B * Hkv * S * (row_bytes / 16);
-  if (total == 0) return hipSuccess;
-  long long blocks = (total + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(kv_append_varlen_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     row_bytes, S, Hkv, B * Hkv, (char*)k_cache, (char*)v_cache, lens, max_len, cap,
-                     (const char*)k_new, (const char*)v_new);
-  return hipGetLastError();
+  return launch_append(elem_bytes, B, Hkv, S, d, k_cache, v_cache, 0, lens, max_len, cap, k_new,
+                       v_new, stream);
 }
 
 }  // namespace e2d2
