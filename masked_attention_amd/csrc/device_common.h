@@ -572,7 +572,7 @@ __device__ __forceinline__ void read_vt_half32(uint32_t vbase, const uint32_t (&
   for (int db = 0; db < NDB; ++db) vf[db] = join_bf16(o[2 * db], o[2 * db + 1]);
 }
 
-// LDS byte address of an LDS pointer.// LDS byte address of an LDS pointer.
+// LDS byte address of an LDS pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void E2D2_LDS* p) {
   return (uint32_t)(uintptr_t)p;
 }
