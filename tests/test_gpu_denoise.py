@@ -1,6 +1,7 @@
 """GPU parity of the denoising step and the KV-cache append against the fp64 oracle
 (needs an MI355X).  Tolerances as in test_gpu_train.py; the append is a bitwise copy.
 """
+import math
 import sys
 
 import numpy as np
@@ -25,13 +26,17 @@ def _workspace(dtype, B, Hq, Hkv, S, d, C):
     return (torch.empty(n, dtype=torch.uint8, device="cuda") if n else None), n
 
 
-def _denoise_case(B, Hq, Hkv, S, d, C, cap, dtype, seed, heads=None, step=0):
-    say(f"[denoise] B{B} Hq{Hq} Hkv{Hkv} S{S} d{d} C{C} cap{cap} {dtype} seed {seed:#x}")
-    q = host((B, Hq, S, d), seed, K.Q_BLK, dtype, step=step)
-    kb = host((B, Hkv, S, d), seed, K.K_BLK, dtype, step=step)
-    vb = host((B, Hkv, S, d), seed, K.V_BLK, dtype, step=step)
-    kc = host((B, Hkv, cap, d), seed, K.K_CACHE, dtype)
-    vc = host((B, Hkv, cap, d), seed, K.V_CACHE, dtype)
+def _denoise_case(B, Hq, Hkv, S, d, C, cap, dtype, seed, heads=None, step=0, inputs=None):
+    say(f"[denoise] B{B} Hq{Hq} Hkv{Hkv} S{S} d{d} C{C} cap{cap} {dtype} seed {seed:#x}"
+        + (" shaped scores" if inputs is not None else ""))
+    if inputs is None:
+        q = host((B, Hq, S, d), seed, K.Q_BLK, dtype, step=step)
+        kb = host((B, Hkv, S, d), seed, K.K_BLK, dtype, step=step)
+        vb = host((B, Hkv, S, d), seed, K.V_BLK, dtype, step=step)
+        kc = host((B, Hkv, cap, d), seed, K.K_CACHE, dtype)
+        vc = host((B, Hkv, cap, d), seed, K.V_CACHE, dtype)
+    else:
+        q, kc, vc, kb, vb = (inputs[n] for n in ("q", "kc", "vc", "kb", "vb"))
     g = [t.cuda() for t in (q, kc, vc, kb, vb)]
     o = torch.full_like(g[0], float("nan"))
     lse = torch.full((B, Hq, S), float("nan"), device="cuda")
@@ -65,6 +70,32 @@ def _denoise_case(B, Hq, Hkv, S, d, C, cap, dtype, seed, heads=None, step=0):
 ])
 def test_denoise_shapes(B, Hq, Hkv, S, d, C, cap, dtype):
     _denoise_case(B, Hq, Hkv, S, d, C, cap, dtype, 0xE2D2D000 + C + S)
+
+
+# The online softmax's rescaling, and the split path's merge of partial results, under
+# scores that climb along the cache: every query row is 16 u plus small noise, u a unit
+# direction per KV head, cache key j is span * sqrt(d) / 16 * (j / C) u plus N(0, 1)
+# noise (the running max rises in most tiles and differs between the key slices that the
+# split path merges), and the block's own keys are N(0, 1).  Span 200 nats in bf16, 8 in
+# fp32 (where the scores' own rounding stays inside the 1e-5 bound).
+@pytest.mark.parametrize("dtype,span,B,C", [
+    ("bf16", 200.0, 1, 4000), ("bf16", 200.0, 8, 700), ("f32", 8.0, 1, 4000),
+])
+def test_rescaling_under_growing_cache_scores(dtype, span, B, C):
+    Hq, Hkv, S, d = 4, 2, 16, 128
+    seed = 0xE2D2DC01
+    g = lambda shape, kind, step=0: host(shape, seed, kind, "f32", step=step).double()
+    u = g((B, Hkv, 1, d), K.K_CACHE, step=1)
+    u = u / u.norm(dim=-1, keepdim=True)
+    j = torch.arange(C, dtype=torch.float64).view(1, 1, C, 1) / C
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inputs = dict(
+        q=16.0 * u.repeat_interleave(Hq // Hkv, dim=1) + 0.1 * g((B, Hq, S, d), K.Q_BLK),
+        kc=span * math.sqrt(d) / 16.0 * j * u + g((B, Hkv, C, d), K.K_CACHE),
+        vc=g((B, Hkv, C, d), K.V_CACHE), kb=g((B, Hkv, S, d), K.K_BLK),
+        vb=g((B, Hkv, S, d), K.V_BLK))
+    inputs = {n: t.to(dt) for n, t in inputs.items()}
+    _denoise_case(B, Hq, Hkv, S, d, C, C, dtype, seed, inputs=inputs)
 
 
 def test_split_path_is_used():

@@ -6,6 +6,7 @@ absolute, fp32 within 1e-5 * max(1, |ref|).  Tile-visit counters must equal the 
 schedule's count and the oracle's brute-force count exactly, and the mask the kernels
 apply is read back exactly through one-hot probes.
 """
+import math
 import sys
 
 import numpy as np
@@ -23,11 +24,17 @@ def say(msg):
     print(msg, file=sys.__stderr__, flush=True)
 
 
-def _train_case(B, Hq, Hkv, L, S, d, dtype, seed, with_enc=True, heads=None, rows=None):
-    say(f"[train] B{B} Hq{Hq} Hkv{Hkv} L{L} S{S} d{d} {dtype} seed {seed:#x} enc={with_enc}")
-    qd = host((B, Hq, L, d), seed, K.Q_DEC, dtype)
-    qe = host((B, Hq, L, d), seed, K.Q_ENC, dtype)
-    kc, vc, kd, vd = (host((B, Hkv, L, d), seed, k, dtype) for k in (K.K_CTX, K.V_CTX, K.K_DEC, K.V_DEC))
+def _train_case(B, Hq, Hkv, L, S, d, dtype, seed, with_enc=True, heads=None, rows=None,
+                inputs=None):
+    say(f"[train] B{B} Hq{Hq} Hkv{Hkv} L{L} S{S} d{d} {dtype} seed {seed:#x} enc={with_enc}"
+        + (" shaped scores" if inputs is not None else ""))
+    if inputs is None:
+        qd = host((B, Hq, L, d), seed, K.Q_DEC, dtype)
+        qe = host((B, Hq, L, d), seed, K.Q_ENC, dtype)
+        kc, vc, kd, vd = (host((B, Hkv, L, d), seed, k, dtype)
+                          for k in (K.K_CTX, K.V_CTX, K.K_DEC, K.V_DEC))
+    else:
+        qd, qe, kc, vc, kd, vd = (inputs[n] for n in ("qd", "qe", "kc", "vc", "kd", "vd"))
     g = {n: t.cuda() for n, t in dict(qd=qd, qe=qe, kc=kc, vc=vc, kd=kd, vd=vd).items()}
     od = torch.full_like(g["qd"], float("nan"))
     oe = torch.full_like(g["qe"], float("nan"))
@@ -212,3 +219,43 @@ def test_bd3lm_single_stack_layer_via_fused_call(dtype):
             check(oe[b, h], ro[b, h, L:], dtype, f"clean o[{b},{h}]")
             check(ld[b, h], rl[b, h, :L], dtype, f"noised lse[{b},{h}]")
             check(le[b, h], rl[b, h, L:], dtype, f"clean lse[{b},{h}]")
+
+
+def _shaped_scores(B, Hq, Hkv, L, d, dtype, seed, span=0.0, amp=1.0):
+    """Seeded inputs with large or growing scores.  Every query row is 16 u plus small
+    noise, u a unit direction per KV head; clean key j is span * sqrt(d) / 16 * (j / L) u
+    plus N(0, 1) noise, noised key j the same with (1 - j / L): scaled scores climb by
+    about span nats along the clean keys (the running max rises in most tiles) and fall
+    along the noised ones.  With span = 0, queries and keys are amp * N(0, 1) instead
+    (score spread amp^2 nats).  Values are N(0, 1)."""
+    g = lambda shape, kind, step=0: host(shape, seed, kind, "f32", step=step).double()
+    dt = TORCH_DT[dtype]
+    if span == 0.0:
+        qd, qe = amp * g((B, Hq, L, d), K.Q_DEC), amp * g((B, Hq, L, d), K.Q_ENC)
+        kc, kd = amp * g((B, Hkv, L, d), K.K_CTX), amp * g((B, Hkv, L, d), K.K_DEC)
+    else:
+        u = g((B, Hkv, 1, d), K.K_CTX, step=1)
+        u = u / u.norm(dim=-1, keepdim=True)
+        uq = u.repeat_interleave(Hq // Hkv, dim=1)
+        bk = span * math.sqrt(d) / 16.0
+        j = torch.arange(L, dtype=torch.float64).view(1, 1, L, 1) / L
+        qd = 16.0 * uq + 0.1 * g((B, Hq, L, d), K.Q_DEC)
+        qe = 16.0 * uq + 0.1 * g((B, Hq, L, d), K.Q_ENC)
+        kc = bk * j * u + g((B, Hkv, L, d), K.K_CTX)
+        kd = bk * (1.0 - j) * u + g((B, Hkv, L, d), K.K_DEC)
+    vc, vd = g((B, Hkv, L, d), K.V_CTX), g((B, Hkv, L, d), K.V_DEC)
+    return {n: t.to(dt) for n, t in dict(qd=qd, qe=qe, kc=kc, vc=vc, kd=kd, vd=vd).items()}
+
+
+# The online softmax's rescaling under scores far from N(0, 1): a running max that rises
+# in most tiles (span 200 nats in bf16; 8 in fp32, which rescales every tile and where
+# the scores' own fp32 rounding stays inside the 1e-5 bound) and large random scores
+# (spread 16 nats in bf16, 2.25 in fp32).
+@pytest.mark.parametrize("dtype,d,span,amp", [
+    ("bf16", 64, 200.0, 1.0), ("bf16", 128, 200.0, 1.0), ("bf16", 64, 0.0, 4.0),
+    ("f32", 64, 8.0, 1.0), ("f32", 32, 0.0, 1.5),
+])
+def test_rescaling_under_large_and_growing_scores(dtype, d, span, amp):
+    B, Hq, Hkv, L, S = 1, 4, 2, 512, 16
+    inputs = _shaped_scores(B, Hq, Hkv, L, d, dtype, 0xE2D20C01, span=span, amp=amp)
+    _train_case(B, Hq, Hkv, L, S, d, dtype, 0xE2D20C01, inputs=inputs)
