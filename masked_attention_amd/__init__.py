@@ -84,8 +84,8 @@ def lib():
     global _LIB
     if _LIB is None:
         if not os.path.exists(library_path):
-            raise RuntimeError(f"{library_path} is not built: run __graft_entry__.build() "
-                               "(hipcc for gfx950) first")
+            raise RuntimeError(f"{library_path} is not built: run python -m "
+                               "masked_attention_amd.build (hipcc for gfx950) first")
         h = ctypes.CDLL(library_path)
         for name, (res, args) in _SIGS.items():
             f = getattr(h, name)

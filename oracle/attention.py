@@ -17,7 +17,7 @@ What is computed (the plain definition, nothing blocked, fused or reordered):
   ([Notes] 方法详解 §2 两种连接方式), and the decoder then has to share its attention
   between the two ([Notes] 局限性).
 
-Readings taken where the pages are silent (also listed in the design doc):
+Readings taken where the pages are silent:
   * scale arrives as a float32 (1/sqrt(d) in the workloads); the oracle uses that
     float32 value exactly, widened to fp64;
   * LSE is the natural-log log-sum-exp of the scaled scores over allowed keys;

@@ -9,7 +9,7 @@ Pages cited, by title and section:
   [BD3]     "Block Diffusion: Interpolating Between Autoregressive and Diffusion
             Language Models", xllm-io paper review.
 
-Readings taken where the pages leave a step open (each is also listed in the design doc):
+Readings taken where the pages leave a step open:
   * blocks start at position 0 and hold S consecutive tokens, the last one may be
     shorter ([BD3] 三 技术架构, 块级分解);
   * inside a block attention is bidirectional; the encoder row sees its own block and

@@ -156,7 +156,7 @@ def _lib():
         import torch  # noqa: F401  (binds the library to the HIP runtime torch has loaded)
 
         if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build()")
+            raise RuntimeError(f"{_LIB_PATH} is not built; run python -m masked_attention_amd.build")
         lib = ctypes.CDLL(_LIB_PATH)
         lib.synth_fill_normal.restype = ctypes.c_int
         lib.synth_fill_normal.argtypes = [
