@@ -21,7 +21,7 @@ Also measured in the same run and reported in the same JSON line:
   * ``cpu_baseline``: the fp64 CPU oracle timed on the host cores on a bounded sample
     of the training workload.
 
-``python bench.py --gpus N --steps K --warmup W``; this build runs on one GPU only.
+``python bench.py --gpus N --steps K --warmup W``; the benchmark runs on one GPU only.
 """
 from __future__ import annotations
 
@@ -530,7 +530,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); "
+        print("bench.py: the benchmark measures one GPU only (no multi-GPU path); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
