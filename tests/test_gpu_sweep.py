@@ -4,8 +4,9 @@ The hand-picked cases in the other files cover each edge on purpose; this sweep 
 shapes at random (fixed seed, so the list is the same on every run) to reach the
 combinations nobody picked: odd and ragged block sizes, lengths that are not tile
 multiples, one to eight query heads per KV head, empty and ragged caches, both dtypes,
-with and without the encoder.  Each case runs through the C-ABI binding and is checked
-element by element with the tolerances of the other GPU tests.
+with and without the encoder, per-sequence cache lengths from empty to full.  Each case
+runs through the C-ABI binding and is checked element by element with the tolerances of
+the other GPU tests.
 """
 import numpy as np
 import pytest
@@ -15,6 +16,7 @@ from helpers import scale_of
 from test_gpu_bwd import NAMES, check_grad, inputs as bwd_inputs, run_gpu as bwd_run
 from test_gpu_denoise import _denoise_case
 from test_gpu_train import _train_case
+from test_gpu_varlen import _varlen_case
 
 pytestmark = pytest.mark.gpu
 
@@ -62,9 +64,27 @@ def _bwd_cases(n):
     return out
 
 
+def _varlen_cases(n):
+    out = []
+    for _ in range(n):
+        Hkv = int(_rng.choice([1, 2]))
+        Hq = Hkv * int(_rng.choice([1, 2, 4, 8]))
+        B = int(_rng.randint(1, 7))
+        S = int(_rng.randint(1, 49))
+        max_len = int(_rng.randint(1, 1500))
+        lens = []
+        for _ in range(B):
+            u = _rng.rand()
+            lens.append(0 if u < 0.15 else max_len if u < 0.3 else int(_rng.randint(1, max_len + 1)))
+        cap = max_len + S + int(_rng.randint(0, 20))
+        out.append((B, Hq, Hkv, S, int(_rng.choice([32, 64, 128])), lens, max_len, cap))
+    return out
+
+
 TRAIN = _train_cases(16)
 DENOISE = _denoise_cases(16)
 BWD = _bwd_cases(10)
+VARLEN = _varlen_cases(10)
 
 
 @pytest.mark.parametrize("i", range(len(TRAIN)))
@@ -88,3 +108,9 @@ def test_sweep_training_backward(i):
                            do_enc=ins[7] if with_enc else None)
     for name, g, r in zip(NAMES, got, ref):
         check_grad(g, r, f"{name} (case {BWD[i]})")
+
+
+@pytest.mark.parametrize("i", range(len(VARLEN)))
+def test_sweep_denoise_step_per_sequence_lengths(i):
+    B, Hq, Hkv, S, d, lens, max_len, cap = VARLEN[i]
+    _varlen_case(B, Hq, Hkv, S, d, lens, max_len, cap, 0xE2D25300 + i)

@@ -39,8 +39,11 @@ def _workspace(B, Hq, Hkv, S, d, C):
     (3, 2, 2, 4, 32, [5, 0, 64], 100, 104),
 ])
 def test_varlen_step_matches_oracle_per_sequence(B, Hq, Hkv, S, d, lens, max_len, cap):
-    seed = 0xE2D20007
-    say(f"[varlen] B{B} Hq{Hq} Hkv{Hkv} S{S} d{d} lens {lens} max {max_len}")
+    _varlen_case(B, Hq, Hkv, S, d, lens, max_len, cap, 0xE2D20007)
+
+
+def _varlen_case(B, Hq, Hkv, S, d, lens, max_len, cap, seed):
+    say(f"[varlen] B{B} Hq{Hq} Hkv{Hkv} S{S} d{d} lens {lens} max {max_len} seed {seed:#x}")
     q, kc, vc, kb, vb = _inputs(B, Hq, Hkv, S, d, cap, seed)
     g = [t.cuda() for t in (q, kc, vc, kb, vb)]
     lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
