@@ -248,6 +248,64 @@ def bench_layer_split(B, H, L, S, d, steps, seed):
     return out
 
 
+def bench_denoise_varlen(steps, seed):
+    """The denoise workload's heads (B32 Hq16 Hkv8 d128, block 32) with a cache length of
+    its own per sequence, drawn once (seeded) from [1024, 2048], read by the kernel from a
+    device array: `steps` steps back to back from one HIP graph, as a decode loop over a
+    ragged batch runs them."""
+    import numpy as np
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, S, max_len = 32, 16, 8, 128, 32, 2048
+    cap = max_len + S
+    lens = np.random.RandomState(seed & 0xFFFFFFFF).randint(1024, max_len + 1, size=B)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+
+    def fill(shape, kind, rows=None, **kw):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        device_fill(t, seed, tensor_id(kind, **kw), rows=rows)
+        return t
+
+    kc = fill((B, Hkv, cap, d), K.K_CACHE, rows=max_len)
+    vc = fill((B, Hkv, cap, d), K.V_CACHE, rows=max_len)
+    qs = [fill((B, Hq, S, d), K.Q_BLK, step=t) for t in range(steps)]
+    ks = [fill((B, Hkv, S, d), K.K_BLK, step=t) for t in range(steps)]
+    vs = [fill((B, Hkv, S, d), K.V_BLK, step=t) for t in range(steps)]
+    o = torch.empty((B, Hq, S, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, S), device=dev)
+    nws = m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, Hq, Hkv, S, d, max_len)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    stream = torch.cuda.current_stream(dev)
+    it = [0]
+
+    def next_step():
+        t = it[0] % steps
+        m.e2d2_attn_denoise_step_varlen(qs[t], kc, vc, lens_t, max_len, ks[t], vs[t], o,
+                                        lse_blk=lse, workspace=ws)
+        it[0] += 1
+
+    g = graph_of(next_step, steps)
+    g.replay()
+    clock_warmup(g.replay)
+    per_step = []
+    for _ in range(4):
+        _, ms = timed_launches(g.replay, 1, stream)
+        per_step.append(ms / steps)
+    us = sorted(per_step)[len(per_step) // 2] * 1e3
+    alg = (int(lens.sum()) * 2 * Hkv * d * 2 + 2 * B * Hkv * S * d * 2 + 2 * B * Hq * S * d * 2
+           + B * Hq * S * 4)
+    gbs = alg / (us * 1e-6) / 1e9
+    return dict(workload="denoise step with per-sequence cache lengths, B32 Hq16 Hkv8 d128 block 32, "
+                         "lengths uniform in [1024, 2048] (seeded), bf16",
+                lens_min=int(lens.min()), lens_mean=round(float(lens.mean()), 1), lens_max=int(lens.max()),
+                us_per_step_warm=round(us, 2), algorithmic_bytes_per_step=alg, gbs_warm=round(gbs, 1),
+                frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+
+
 def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
     import torch
 
@@ -580,6 +638,9 @@ def main():
         print(f"[bench] denoise: warm {out['denoise']['us_per_step_warm']:.1f} us "
               f"({out['denoise']['gbs_warm']:.0f} GB/s), cold {out['denoise']['us_per_step_cold']:.1f} us "
               f"({out['denoise']['gbs_cold']:.0f} GB/s)", file=sys.stderr, flush=True)
+        out["denoise_varlen"] = bench_denoise_varlen(32, 0xE2D20009)
+        print(f"[bench] denoise varlen: {out['denoise_varlen']['us_per_step_warm']:.1f} us "
+              f"({out['denoise_varlen']['gbs_warm']:.0f} GB/s)", file=sys.stderr, flush=True)
 
     if args.only in ("all", "declayer"):
         out["decoder_layer"] = bench_decoder_layer(32, 5, 0xE2D20003)
