@@ -601,13 +601,20 @@ __device__ __forceinline__ BufDesc buf_desc(const void* base, uint32_t bytes) {
 }
 // 16 (dma_lds16) or 4 (dma_lds4) bytes per lane from buffer offset voff + soff into
 // LDS at lds + 16 * lane (4 * lane); lds and soff wave-uniform.
+// Each call sets m0 (the LDS base of a buffer_load ... lds) itself, with the one wait
+// state the ISA requires between an SALU write of m0 and a load that reads it, and
+// leaves m0 changed.  The compiler reserves m0 and cannot be told of that (a clobber of a
+// reserved register is not honoured), so these helpers go only into kernels where the
+// compiler emits no m0 user of its own: no builtin LDS-DMA (TileLoader), no m0-indexed
+// register access.  The kernels that use them (the projection GEMM, the dK/dV kernel)
+// satisfy this; their generated code has no m0 access outside these asm blocks.
 __device__ __forceinline__ void dma_lds16(BufDesc d, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(d), "s"(soff), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(d), "s"(soff), "s"(lds) : "memory");
 }
 __device__ __forceinline__ void dma_lds4(BufDesc d, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(d), "s"(soff), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(d), "s"(soff), "s"(lds) : "memory");
 }
 // TileLoader's layout and work split, loads issued with dma_lds16.
 template <int D, int ROWS, int NWAVES>
