@@ -8,6 +8,8 @@ with and without the encoder, per-sequence cache lengths from empty to full.  Ea
 runs through the C-ABI binding and is checked element by element with the tolerances of
 the other GPU tests.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -81,10 +83,13 @@ def _varlen_cases(n):
     return out
 
 
-TRAIN = _train_cases(16)
-DENOISE = _denoise_cases(16)
-BWD = _bwd_cases(10)
-VARLEN = _varlen_cases(10)
+# E2D2_SWEEP_SCALE=k draws k times as many cases (the first ones stay the same only for
+# k = 1: the draws interleave); the default keeps the suite to a few seconds.
+_K = max(1, int(os.environ.get("E2D2_SWEEP_SCALE", "1")))
+TRAIN = _train_cases(16 * _K)
+DENOISE = _denoise_cases(16 * _K)
+BWD = _bwd_cases(10 * _K)
+VARLEN = _varlen_cases(10 * _K)
 
 
 @pytest.mark.parametrize("i", range(len(TRAIN)))
