@@ -87,6 +87,29 @@ e2d2_status e2d2_attn_encoder_blockcausal(int dtype, int B, int Hq, int Hkv, int
                                           const void* v, void* o, float* lse,
                                           unsigned long long* dbg_tile_visits, void* stream);
 
+/* Prompt encoding for a batch of prompts of different lengths ([Notes] 方法详解 §3
+ * 采样算法: sampling starts by running the encoder over the prompt to build its KV
+ * cache).  Sequence b's prompt holds lens[b] tokens and is blocked like the training
+ * encoder (blocks of S from position 0, the last one possibly shorter): its row i
+ * attends its keys j < lens[b] with blk(j) <= blk(i).
+ *   q, o [B][Hq][L][d]: rows [0, lens[b]) of sequence b are read / written, the rest of
+ *   o and lse is left untouched; lse [B][Hq][L] or NULL.
+ *   k, v [B][Hkv][kv_rows][d], kv_rows >= L: rows [0, lens[b]) hold the prompt's keys
+ *   and values.  With kv_rows = the cache capacity these are the KV-cache buffers of
+ *   e2d2_attn_denoise_step: a projection writes the prompt's K/V straight into the
+ *   cache, this call reads them there, and no append follows.
+ *   lens: device array of B int32 (4-byte aligned), read when the kernel runs (a
+ *   captured HIP graph stays valid while the caller updates it on the device); each
+ *   length is clamped to [0, L].  L is the host bound that sizes the launch.
+ * bf16 only (fp32: E2D2_ERR_UNSUPPORTED).  Errors as e2d2_attn_encoder_blockcausal,
+ * plus E2D2_ERR_NULL for a NULL lens and E2D2_ERR_SHAPE for kv_rows < L. */
+e2d2_status e2d2_attn_encoder_blockcausal_varlen(int dtype, int B, int Hq, int Hkv, int L, int d,
+                                                 int S, float scale, const void* q, const void* k,
+                                                 const void* v, long long kv_rows,
+                                                 const int* lens, void* o, float* lse,
+                                                 unsigned long long* dbg_tile_visits,
+                                                 void* stream);
+
 /* Training forward of the fused decoder self+cross attention ([Notes] §4 训练算法 and
  * §2 两种连接方式): noised query i attends, under ONE softmax, the clean context keys
  * j of strictly earlier blocks (blk(j) < blk(i)) and the noised keys j of its own
@@ -142,6 +165,12 @@ size_t e2d2_attn_denoise_workspace_bytes(int dtype, int B, int Hq, int Hkv, int 
 /* One denoising step ([Notes] §3 采样算法; [Summary] "Methodology in Plain English"):
  * the S queries of the current [MASK] block attend every cached clean key
  * (rows [0, cache_len) of the cache) and every key of their own block, with no mask.
+ * The same call is the encoder's update of a finished block ([Notes] §3: the finished
+ * block goes through the encoder, which extends the KV cache): with q_blk the encoder
+ * queries of the block's S clean tokens and k_blk, v_blk the encoder's keys/values of
+ * the block, its rows equal the training encoder's rows of that block (a clean token
+ * sees its own block and every earlier one); k_blk, v_blk are then what
+ * e2d2_kv_cache_append adds to the cache.
  *   q_blk [B][Hq][S][d]; k_cache, v_cache [B][Hkv][cache_cap][d] (rows beyond
  *   cache_len are not read); k_blk, v_blk [B][Hkv][S][d] this step's own-block K/V;
  *   o_blk [B][Hq][S][d]; lse_blk [B][Hq][S] or NULL.

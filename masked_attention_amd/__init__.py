@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "E2D2Error", "lib", "library_path", "abi_version",
-    "e2d2_attn_encoder_blockcausal", "e2d2_attn_train_fwd", "e2d2_attn_denoise_step",
+    "e2d2_attn_encoder_blockcausal", "e2d2_attn_encoder_blockcausal_varlen",
+    "e2d2_attn_train_fwd", "e2d2_attn_denoise_step",
     "e2d2_attn_denoise_workspace_bytes", "e2d2_kv_cache_append", "e2d2_attn_tile_shape",
     "e2d2_attn_count_tiles", "e2d2_attn_denoise_step_varlen", "e2d2_kv_cache_append_varlen",
     "e2d2_attn_train_bwd", "e2d2_attn_train_bwd_workspace_bytes",
@@ -46,6 +47,8 @@ _SIGS = {
     "e2d2_last_hip_error": (_i, []),
     "e2d2_attn_encoder_blockcausal": (_i, [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp]),
+    "e2d2_attn_encoder_blockcausal_varlen": (_i, [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp,
+                                                  _ll, _vp, _vp, _vp, _vp, _vp]),
     "e2d2_attn_train_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp]),
     "e2d2_attn_denoise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _ll]),
@@ -158,6 +161,26 @@ def e2d2_attn_encoder_blockcausal(q, k, v, o, S: int, lse=None, scale=None, tile
         _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _opt(lse, "lse", 3),
         _opt(tile_visits, "tile_visits", 1), _stream(q))
     _check("e2d2_attn_encoder_blockcausal", st)
+
+
+def e2d2_attn_encoder_blockcausal_varlen(q, k, v, lens, o, S: int, lse=None, scale=None,
+                                         tile_visits=None):
+    """Prompt encoding with per-sequence lengths: q/o [B, Hq, L, d]; k/v [B, Hkv, kv_rows,
+    d] (kv_rows >= L, e.g. the KV-cache buffers); ``lens`` an int32 CUDA tensor [B] read
+    on the device.  Sequence b's rows [0, lens[b]) attend its keys [0, lens[b]) under
+    the block-causal mask; the rest of o and lse is left untouched (bf16 only)."""
+    B, Hq, L, d = q.shape
+    Hkv, kv_rows = k.shape[1], k.shape[2]
+    _same(q.dtype, k, v, o)
+    if tuple(k.shape) != (B, Hkv, kv_rows, d) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, L)):
+        raise ValueError("lse must be float32 [B, Hq, L]")
+    st = lib().e2d2_attn_encoder_blockcausal_varlen(
+        _dtype_code(q), B, Hq, Hkv, L, d, int(S), _default_scale(d, scale), _dev(q, "q"),
+        _dev(k, "k"), _dev(v, "v"), kv_rows, _lens(lens, B), _dev(o, "o"), _opt(lse, "lse", 3),
+        _opt(tile_visits, "tile_visits", 1), _stream(q))
+    _check("e2d2_attn_encoder_blockcausal_varlen", st)
 
 
 def e2d2_attn_train_fwd(q_dec, k_ctx, v_ctx, k_dec, v_dec, o_dec, S: int, lse_dec=None,

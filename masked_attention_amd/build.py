@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -39,6 +40,44 @@ def _run(cmd):
     return err
 
 
+# ---- m0 guard.  dma_lds16 / dma_lds4 (device_common.h) write m0, the LDS base of a
+# buffer_load ... lds, from inline asm, which the compiler cannot be told about (it
+# reserves m0).  That is sound only in a kernel where the compiler itself emits no m0
+# access.  Every kernel's generated AMD assembly is checked: in a kernel holding such an
+# asm block, each m0-writing block must be exactly the helper's sequence, and no other
+# instruction may name m0 or read it implicitly.
+_ASM_BLOCK = re.compile(r";;#ASMSTART\n(.*?)\n\s*;;#ASMEND", re.S)
+_DMA_SEQ = re.compile(r"\s*s_mov_b32 m0, s\d+\s*\n\s*s_nop 0\s*\n"
+                      r"\s*buffer_load_dword(x4)? v\d+, s\[\d+:\d+\], s\d+ offen lds\s*$")
+# instructions that read m0 without naming it
+_M0_IMPLICIT = re.compile(r"\b(s_sendmsg\w*|s_movrel\w*|v_movrel\w*|ds_gws\w*|ds_append|"
+                          r"ds_consume|ds_\w*addtid\w*|v_interp\w*|global_load_lds\w*)\b|"
+                          r"\slds\s*$")
+
+
+def check_m0(asm: str, what: str) -> int:
+    """Raise when a kernel of ``asm`` mixes the asm m0 writes with any other m0 use.
+    Returns the number of kernels holding the asm sequence."""
+    n = 0
+    starts = [mm.start() for mm in re.finditer(r"^\S+:\s*;\s*@", asm, re.M)] + [len(asm)]
+    for a, b in zip(starts, starts[1:]):
+        body = asm[a:b]
+        name = body.split(":", 1)[0]
+        blocks = [x for x in _ASM_BLOCK.findall(body) if re.search(r"\bm0\b", x)]
+        if not blocks:
+            continue
+        n += 1
+        for x in blocks:
+            if not _DMA_SEQ.fullmatch(x):
+                raise RuntimeError(f"{what}: {name}: unexpected m0 asm block:\n{x}")
+        for line in _ASM_BLOCK.sub("", body).splitlines():
+            code = line.split(";", 1)[0]
+            if re.search(r"\bm0\b", code) or _M0_IMPLICIT.search(code):
+                raise RuntimeError(f"{what}: {name} writes m0 from asm and also has the "
+                                   f"compiler's m0 use: {line.strip()}")
+    return n
+
+
 def build(verbose: bool = False) -> None:
     """Compile both libraries (always; never skips on existing outputs)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -48,12 +87,24 @@ def build(verbose: bool = False) -> None:
         jobs.append((obj, [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]))
     synth_obj = os.path.join(BUILD_DIR, "synth_fill.o")
     jobs.append((synth_obj, [HIPCC, *COMMON, "-c", SYNTH_SRC, "-o", synth_obj]))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        futs = [ex.submit(_run, cmd) for _, cmd in jobs]
+    asm_jobs = []
+    for src in SOURCES:
+        out = os.path.join(BUILD_DIR, src.replace(".hip", ".s"))
+        asm_jobs.append((out, [HIPCC, *COMMON, "--cuda-device-only", "-S",
+                               os.path.join(CSRC, src), "-o", out]))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        futs = [ex.submit(_run, cmd) for _, cmd in jobs + asm_jobs]
         for f in futs:
             msg = f.result()
             if verbose and msg:
                 print(msg, file=sys.stderr)
+    n_dma = 0
+    for out, _ in asm_jobs:
+        with open(out) as f:
+            n_dma += check_m0(f.read(), os.path.basename(out))
+    if n_dma == 0:
+        raise RuntimeError("m0 guard found no kernel with the asm LDS-DMA sequence; "
+                           "the assembly format it parses may have changed")
     objs = [o for o, _ in jobs[:-1]]
     tmp = LIB + ".tmp"
     _run([HIPCC, *COMMON, "-shared", *objs, "-o", tmp])

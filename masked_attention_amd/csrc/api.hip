@@ -122,6 +122,7 @@ e2d2_status e2d2_attn_encoder_blockcausal(int dtype, int B, int Hq, int Hkv, int
     p.kinds[0] = p.kinds[1] = e2d2::kEnc;
     p.n_kinds = 1;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
+    p.kv_rows = L;
     p.n_qtiles = cdiv(L, e2d2::train_tile_bm(d));
     p.xcd_groups = (B * Hq) % 8 == 0;
     p.scale = scale;
@@ -141,6 +142,39 @@ e2d2_status e2d2_attn_encoder_blockcausal(int dtype, int B, int Hq, int Hkv, int
   p.n_kinds = 1;
   p.n_qtiles = cdiv(L, e2d2::kF32TileBM);
   return hip_status(e2d2::launch_attn_f32(p, d, s));
+}
+
+e2d2_status e2d2_attn_encoder_blockcausal_varlen(int dtype, int B, int Hq, int Hkv, int L, int d,
+                                                 int S, float scale, const void* q, const void* k,
+                                                 const void* v, long long kv_rows,
+                                                 const int* lens, void* o, float* lse,
+                                                 unsigned long long* dbg_tile_visits,
+                                                 void* stream) {
+  e2d2_status st = check_train_shape(dtype, B, Hq, Hkv, L, d, S, scale);
+  if (st != E2D2_OK) return st;
+  if (dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
+  if (kv_rows < L || kv_rows > kMaxLen || !slice_ok(kv_rows, d)) return E2D2_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lens) return E2D2_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lens) ||
+      (lse && !aligned4(lse)) || (dbg_tile_visits && ((uintptr_t)dbg_tile_visits & 7u)))
+    return E2D2_ERR_SHAPE;
+  e2d2::TrainParams p = {};
+  p.q[0] = (const __bf16*)q;
+  p.o[0] = (__bf16*)o;
+  p.lse[0] = lse;
+  p.k[0] = p.k[1] = (const __bf16*)k;
+  p.v[0] = p.v[1] = (const __bf16*)v;
+  p.kinds[0] = p.kinds[1] = e2d2::kEnc;
+  p.n_kinds = 1;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
+  p.kv_rows = (int)kv_rows;
+  p.lens = lens;
+  p.n_qtiles = cdiv(L, e2d2::train_tile_bm(d));
+  p.xcd_groups = (B * Hq) % 8 == 0;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  p.visits = dbg_tile_visits;
+  return hip_status(e2d2::launch_train_bf16(p, d, (hipStream_t)stream));
 }
 
 e2d2_status e2d2_attn_train_fwd(int dtype, int B, int Hq, int Hkv, int L, int d, int S, float scale,
@@ -176,6 +210,7 @@ e2d2_status e2d2_attn_train_fwd(int dtype, int B, int Hq, int Hkv, int L, int d,
     p.kinds[1] = e2d2::kEnc;
     p.n_kinds = with_enc ? 2 : 1;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.S = S;
+    p.kv_rows = L;
     p.n_qtiles = cdiv(L, e2d2::train_tile_bm(d));
     p.xcd_groups = (B * Hq * p.n_kinds) % 8 == 0;
     p.scale = scale;
@@ -313,15 +348,15 @@ e2d2_status denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float 
       (cache_len > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) ||
       (lse_blk && !aligned4(lse_blk)) || (dbg_tile_visits && ((uintptr_t)dbg_tile_visits & 7u)))
     return E2D2_ERR_SHAPE;
-  const size_t need = denoise_ws_bytes(dtype, B, Hq, Hkv, S, d, cache_len);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
-    return E2D2_ERR_WORKSPACE;
   if (dtype == E2D2_BF16) {
     const DenoiseShape sh = denoise_shape(B, Hq, Hkv, S, cache_len);
     if ((long long)B * Hkv * sh.n_qgroups * sh.n_split > INT32_MAX) return E2D2_ERR_SHAPE;
   } else if ((long long)B * Hq * cdiv(S, e2d2::kF32TileBM) > INT32_MAX) {
     return E2D2_ERR_SHAPE;
   }
+  const size_t need = denoise_ws_bytes(dtype, B, Hq, Hkv, S, d, cache_len);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return E2D2_ERR_WORKSPACE;
   if (!launch) return E2D2_OK;
   hipStream_t s = (hipStream_t)stream;
   // An empty cache has no rows to read; any non-NULL pointer stands in.

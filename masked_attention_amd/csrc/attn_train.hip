@@ -106,9 +106,13 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   const int b = bh / p.Hq;
   const int hq = bh % p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
-  const int L = p.L, S = p.S;
+  const int S = p.S;
+  // this sequence's length: all L rows, or (per-sequence lengths on the device) its own
+  // prefix of them; the row stride of q, o and lse stays p.L
+  const int L = p.lens != nullptr ? min(max(p.lens[b], 0), p.L) : p.L;
 
   const int q0 = qtile * kBM;
+  if (q0 >= L) return;  // the whole query tile lies past this sequence's end
   const int r_last = min(q0 + kBM, L) - 1;
   const int nsrc = num_sources(kind);
   const TileRange tr0 = visited_tiles(kind, 0, q0, r_last, S, L, 0, kBN);
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   const int n0 = tr0.last - tr0.first;
   const int ntot = n0 + (tr1.last - tr1.first);
 
-  const size_t kv_off = ((size_t)b * p.Hkv + hk) * (size_t)L * D;
+  const size_t kv_off = ((size_t)b * p.Hkv + hk) * (size_t)p.kv_rows * D;
   const uint32_t kv_bytes = (uint32_t)L * D * 2u;
   const __amdgpu_buffer_rsrc_t rk0 = make_rsrc(p.k[0] + kv_off, kv_bytes);
   const __amdgpu_buffer_rsrc_t rv0 = make_rsrc(p.v[0] + kv_off, kv_bytes);
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     }
   };
 
-  const size_t q_off = ((size_t)b * p.Hq + hq) * (size_t)L * D;
+  const size_t q_off = ((size_t)b * p.Hq + hq) * (size_t)p.L * D;
   bf16x8 qf[NC];
   {
     const __bf16* qrow = p.q[slot] + q_off + (size_t)(row_ok ? qi : 0) * D + ((lane >> 5) << 3);
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
         *(bf16x4*)(orow + d) = v;
       }
     if (p.lse[slot] != nullptr && lane < 32)
-      p.lse[slot][((size_t)b * p.Hq + hq) * L + qi] =
+      p.lse[slot][((size_t)b * p.Hq + hq) * p.L + qi] =
           (ms + __log2f(l_tot)) * 0.6931471805599453f;
   }
   if (p.visits != nullptr && threadIdx.x == 0) atomicAdd(p.visits, (unsigned long long)ntot);

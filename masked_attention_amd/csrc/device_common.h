@@ -338,7 +338,7 @@ __device__ __forceinline__ void tr_reads1(const uint32_t (&a)[8], long (&o)[8]) 
       : "memory");
 }
 
-// Batched 16-byte LDS reads (the K operands of S^T = K Q^T), in one asm block that// Batched 16-byte LDS reads (the K operands of S^T = K Q^T), in one asm block that
+// Batched 16-byte LDS reads (the K operands of S^T = K Q^T), in one asm block that
 // waits for them, so one LDS round trip covers a whole batch of MFMAs instead of one
 // each.  kreadN<OFF>: o[i] = 16 bytes at a[i] + OFF.
 template <int OFF>
@@ -606,8 +606,9 @@ __device__ __forceinline__ BufDesc buf_desc(const void* base, uint32_t bytes) {
 // leaves m0 changed.  The compiler reserves m0 and cannot be told of that (a clobber of a
 // reserved register is not honoured), so these helpers go only into kernels where the
 // compiler emits no m0 user of its own: no builtin LDS-DMA (TileLoader), no m0-indexed
-// register access.  The kernels that use them (the projection GEMM, the dK/dV kernel)
-// satisfy this; their generated code has no m0 access outside these asm blocks.
+// register access.  The build enforces this on the generated AMD assembly of every
+// kernel (masked_attention_amd/build.py, check_m0) and fails when a kernel holding these
+// blocks has any other m0 access.
 __device__ __forceinline__ void dma_lds16(BufDesc d, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(d), "s"(soff), "s"(lds) : "memory");

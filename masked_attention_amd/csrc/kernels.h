@@ -18,6 +18,8 @@ struct TrainParams {
   int kinds[2];
   int n_kinds;
   int B, Hq, Hkv, L, S;
+  int kv_rows;      // rows per (batch, kv head) of the K/V buffers (L, or a cache capacity)
+  const int* lens;  // per-sequence lengths [B] on the device (clamped to [0, L]), or NULL: all L
   int n_qtiles;
   int xcd_groups;  // 1: (B*Hq*n_kinds) % 8 == 0, heads grouped per XCD
   float scale;     // softmax scale

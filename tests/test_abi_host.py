@@ -149,6 +149,26 @@ def test_denoise_workspace_sizes():
     assert m.e2d2_attn_denoise_workspace_bytes(m.BF16, 1, 2, 3, 4, 128, 4096) == 0  # invalid
 
 
+def _enc_varlen(**kw):
+    a = dict(dtype=m.BF16, B=2, Hq=2, Hkv=1, L=64, d=64, S=8, scale=0.125, q=16, k=16, v=16,
+             kv_rows=80, lens=16, o=16, lse=None, dbg=None, stream=None)
+    a.update(kw)
+    return m.lib().e2d2_attn_encoder_blockcausal_varlen(*a.values())
+
+
+def test_encoder_varlen_validation_returns_before_launch():
+    assert _enc_varlen(lens=None) == ERR_NULL
+    assert _enc_varlen(k=None) == ERR_NULL
+    assert _enc_varlen(lens=18) == ERR_SHAPE      # misaligned int32 array
+    assert _enc_varlen(kv_rows=63) == ERR_SHAPE   # K/V rows fewer than the query rows
+    assert _enc_varlen(kv_rows=(1 << 24) + 1) == ERR_SHAPE
+    assert _enc_varlen(dtype=m.F32) == ERR_UNSUPPORTED
+    assert _enc_varlen(d=96) == ERR_UNSUPPORTED
+    assert _enc_varlen(S=0) == ERR_SHAPE
+    assert _enc_varlen(Hq=3, Hkv=2) == ERR_SHAPE
+    assert _enc_varlen(o=40) == ERR_SHAPE         # misaligned
+
+
 def test_append_validation():
     lib = m.lib()
     assert lib.e2d2_kv_cache_append(m.BF16, 1, 1, 4, 64, 16, 16, 10, 12, 16, 16, None) == ERR_CAPACITY

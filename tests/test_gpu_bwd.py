@@ -15,7 +15,7 @@ import torch
 
 import masked_attention_amd as m
 import oracle
-from helpers import TensorKind as K, host, scale_of
+from helpers import TensorKind as K, gpu_fill, host, scale_of
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +123,32 @@ def test_bwd_is_deterministic():
     b = run_gpu(ins, S, True)
     for name, x, y in zip(NAMES, a, b):
         assert torch.equal(x, y), name
+
+
+@pytest.mark.timeout(900)
+def test_bwd_long_training_workload_sampled_heads():
+    # B2 Hq16/Hkv8 d128 L8192 S64 (the long training workload), encoder included: every
+    # gradient is computed on the GPU in the launch configuration the bench times; two
+    # (batch, kv head) groups -- each with both of its query heads -- are checked
+    # element by element against the oracle.  Inputs are drawn on the device
+    # (bit-identical to the host generator) and copied back for the oracle.
+    B, Hq, Hkv, L, S, d = 2, 16, 8, 8192, 64, 128
+    seed = 0xE2D2B400
+    say(f"[bwd] long B{B} Hq{Hq}/{Hkv} L{L} S{S} d{d}")
+    q, kv = (B, Hq, L, d), (B, Hkv, L, d)
+    kinds = [(K.Q_DEC, q), (K.K_CTX, kv), (K.V_CTX, kv), (K.K_DEC, kv), (K.V_DEC, kv),
+             (K.Q_ENC, q), (K.DO_DEC, q), (K.DO_ENC, q)]
+    dev = [gpu_fill(shape, seed, kind, "bf16") for kind, shape in kinds]
+    got = run_gpu(dev, S, True)
+    got = [t.cpu() for t in got]
+    ins = [t.cpu() for t in dev]
+    del dev
+    heads = [(0, 0), (1, 7)]
+    ref = oracle.train_bwd(*ins[:5], S, scale_of(d), ins[6], q_enc=ins[5], do_enc=ins[7],
+                           kv_heads=heads)
+    g = Hq // Hkv
+    for b, hk in heads:
+        for name, x, r in zip(NAMES, got, ref):
+            hs = range(hk * g, (hk + 1) * g) if name.startswith("dq") else [hk]
+            for h in hs:
+                check_grad(x[b, h], r[b, h], f"{name}[{b},{h}]")
