@@ -185,6 +185,26 @@ e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int
                                    void* workspace, size_t workspace_bytes,
                                    unsigned long long* dbg_tile_visits, void* stream);
 
+/* e2d2_attn_denoise_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step and arguments without the workspace.  When the step splits its key axis, the
+ * partial results go to a scratch buffer the library owns, a fixed 17 MiB array in
+ * device memory that every GPU the library runs on holds until the process ends (it
+ * covers the largest workspace e2d2_attn_denoise_workspace_bytes returns for any
+ * shape; a larger need would return E2D2_ERR_WORKSPACE).  Its address on the current
+ * device is looked up on the first call there, so that call must not itself be under
+ * stream capture.  Nothing is allocated or freed.  Every call on one GPU shares that
+ * GPU's scratch, so calls that may overlap on one GPU (different streams, no ordering
+ * between them) race and corrupt each other's results; calls ordered on one stream do
+ * not.  The scratch's contents are ignored on entry.  Errors as e2d2_attn_denoise_step,
+ * plus E2D2_ERR_HIP when the scratch cannot be located. */
+e2d2_status e2d2_attn_denoise_step_noalloc(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                           float scale, const void* q_blk, const void* k_cache,
+                                           const void* v_cache, long long cache_len,
+                                           long long cache_cap, const void* k_blk,
+                                           const void* v_blk, void* o_blk, float* lse_blk,
+                                           unsigned long long* dbg_tile_visits, void* stream);
+
 /* KV-cache append after a block is finished ([Notes] §3 采样算法: the finished block
  * goes through the encoder, which updates the KV cache): copies k_new, v_new
  * [B][Hkv][S][d] into rows [cache_len, cache_len + S) of k_cache, v_cache

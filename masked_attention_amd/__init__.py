@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "E2D2Error", "lib", "library_path", "abi_version",
     "e2d2_attn_encoder_blockcausal", "e2d2_attn_encoder_blockcausal_varlen",
-    "e2d2_attn_train_fwd", "e2d2_attn_denoise_step",
+    "e2d2_attn_train_fwd", "e2d2_attn_denoise_step", "e2d2_attn_denoise_step_noalloc",
     "e2d2_attn_denoise_workspace_bytes", "e2d2_kv_cache_append", "e2d2_attn_tile_shape",
     "e2d2_attn_count_tiles", "e2d2_attn_denoise_step_varlen", "e2d2_kv_cache_append_varlen",
     "e2d2_attn_train_bwd", "e2d2_attn_train_bwd_workspace_bytes",
@@ -54,6 +54,8 @@ _SIGS = {
     "e2d2_attn_denoise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _ll]),
     "e2d2_attn_denoise_step": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _ll, _ll, _vp, _vp,
                                     _vp, _vp, _vp, _sz, _vp, _vp]),
+    "e2d2_attn_denoise_step_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _ll, _ll,
+                                            _vp, _vp, _vp, _vp, _vp, _vp]),
     "e2d2_kv_cache_append": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _ll, _ll, _vp, _vp, _vp]),
     "e2d2_attn_denoise_step_varlen": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _ll, _ll,
                                            _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
@@ -285,6 +287,28 @@ def e2d2_attn_denoise_step(q_blk, k_cache, v_cache, cache_len: int, k_blk, v_blk
         _opt(lse_blk, "lse_blk", 3), ws_ptr, ws_bytes, _opt(tile_visits, "tile_visits", 1),
         _stream(q_blk))
     _check("e2d2_attn_denoise_step", st)
+
+
+def e2d2_attn_denoise_step_noalloc(q_blk, k_cache, v_cache, cache_len: int, k_blk, v_blk, o_blk,
+                                   lse_blk=None, scale=None, tile_visits=None):
+    """e2d2_attn_denoise_step without a workspace argument: when the step splits its key
+    axis, the partials go to the library's own fixed device scratch (nothing is
+    allocated).  Calls that may overlap on one GPU race on that scratch."""
+    B, Hq, S, d = q_blk.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    _same(q_blk.dtype, k_cache, v_cache, k_blk, v_blk, o_blk)
+    if tuple(k_cache.shape) != (B, Hkv, cap, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, cap, d]")
+    if tuple(k_blk.shape) != (B, Hkv, S, d) or v_blk.shape != k_blk.shape or o_blk.shape != q_blk.shape:
+        raise ValueError("shape mismatch")
+    if lse_blk is not None and (lse_blk.dtype != torch.float32 or tuple(lse_blk.shape) != (B, Hq, S)):
+        raise ValueError("lse must be float32 [B, Hq, S]")
+    st = lib().e2d2_attn_denoise_step_noalloc(
+        _dtype_code(q_blk), B, Hq, Hkv, S, d, _default_scale(d, scale), _dev(q_blk, "q_blk"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), int(cache_len), cap,
+        _dev(k_blk, "k_blk"), _dev(v_blk, "v_blk"), _dev(o_blk, "o_blk"),
+        _opt(lse_blk, "lse_blk", 3), _opt(tile_visits, "tile_visits", 1), _stream(q_blk))
+    _check("e2d2_attn_denoise_step_noalloc", st)
 
 
 def _lens(cache_lens, B):

@@ -333,7 +333,7 @@ e2d2_status denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float 
                          const void* k_blk, const void* v_blk, void* o_blk, float* lse_blk,
                          void* workspace, size_t workspace_bytes,
                          unsigned long long* dbg_tile_visits, void* stream,
-                         bool launch = true) {
+                         bool launch = true, bool own_scratch = false) {
   if (dtype != E2D2_F32 && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
   if (lens != nullptr && dtype != E2D2_BF16) return E2D2_ERR_UNSUPPORTED;
   if (!head_dim_ok(d)) return E2D2_ERR_UNSUPPORTED;
@@ -355,6 +355,14 @@ e2d2_status denoise_step(int dtype, int B, int Hq, int Hkv, int S, int d, float 
     return E2D2_ERR_SHAPE;
   }
   const size_t need = denoise_ws_bytes(dtype, B, Hq, Hkv, S, d, cache_len);
+  if (own_scratch && need > 0) {
+    // the library's own device scratch (no allocation): its address on this device
+    size_t have = 0;
+    const hipError_t e = e2d2::denoise_scratch(&workspace, &have);
+    if (e != hipSuccess) return hip_status(e);
+    if (need > have) return E2D2_ERR_WORKSPACE;
+    workspace_bytes = have;
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return E2D2_ERR_WORKSPACE;
   if (!launch) return E2D2_OK;
@@ -423,6 +431,17 @@ e2d2_status e2d2_attn_denoise_step(int dtype, int B, int Hq, int Hkv, int S, int
   return denoise_step(dtype, B, Hq, Hkv, S, d, scale, q_blk, k_cache, v_cache, nullptr, cache_len,
                       cache_cap, k_blk, v_blk, o_blk, lse_blk, workspace, workspace_bytes,
                       dbg_tile_visits, stream);
+}
+
+e2d2_status e2d2_attn_denoise_step_noalloc(int dtype, int B, int Hq, int Hkv, int S, int d,
+                                           float scale, const void* q_blk, const void* k_cache,
+                                           const void* v_cache, long long cache_len,
+                                           long long cache_cap, const void* k_blk,
+                                           const void* v_blk, void* o_blk, float* lse_blk,
+                                           unsigned long long* dbg_tile_visits, void* stream) {
+  return denoise_step(dtype, B, Hq, Hkv, S, d, scale, q_blk, k_cache, v_cache, nullptr, cache_len,
+                      cache_cap, k_blk, v_blk, o_blk, lse_blk, nullptr, 0, dbg_tile_visits, stream,
+                      true, true);
 }
 
 e2d2_status e2d2_attn_denoise_step_varlen(int dtype, int B, int Hq, int Hkv, int S, int d,

@@ -32,6 +32,8 @@
 //     split over workgroups; each split writes its partial to the workspace and a
 //     small combine kernel merges them (same fixed order, so results are
 //     deterministic).
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
@@ -393,7 +395,40 @@ hipError_t launch_append(int elem_bytes, int B, int Hkv, int S, int d, void* k_c
   return hipGetLastError();
 }
 
+// Device scratch of the allocation-free denoise call: the split partials (ws_o, ws_ml)
+// live here instead of in a caller workspace.  Its size covers every shape: a split is
+// used only when units = B * Hkv * query groups < 256, with at most ceil(256 / units)
+// splits, so units * splits <= 510 and the workspace holds at most 510 * 64 rows of
+// d + 2 <= 130 floats (16.97 MB).  Each GPU the library runs on holds its own copy until
+// the process ends.
+constexpr size_t kScratchBytes = (size_t)17 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
 }  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t denoise_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // The host-side name `scratch` is not a device address: the runtime gives the
+    // address of this device's copy.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
 
 int denoise_splits(int B, int Hkv, int n_qgroups, int n_tiles) {
   const long long units = (long long)B * Hkv * n_qgroups;

@@ -130,6 +130,9 @@ hipError_t launch_attn_f32(const F32Params& p, int d, hipStream_t stream);
 hipError_t launch_denoise_bf16(const DenoiseParams& p, int d, hipStream_t stream);
 // Denoise split sizing shared by the workspace query and the launch.
 int denoise_splits(int B, int Hkv, int n_qgroups, int n_tiles);
+// Device address (on the current device) and size of the library's own denoise scratch
+// buffer, looked up once per device.
+hipError_t denoise_scratch(void** ptr, size_t* bytes);
 hipError_t launch_kv_append(int elem_bytes, int B, int Hkv, int S, int d, void* k_cache,
                             void* v_cache, long long cache_len, long long cap,
                             const void* k_new, const void* v_new, hipStream_t stream);

@@ -149,6 +149,23 @@ def test_denoise_workspace_sizes():
     assert m.e2d2_attn_denoise_workspace_bytes(m.BF16, 1, 2, 3, 4, 128, 4096) == 0  # invalid
 
 
+def _noalloc(**kw):
+    a = dict(dtype=m.BF16, B=1, Hq=2, Hkv=1, S=4, d=128, scale=0.1, q=16, kc=16, vc=16, C=8,
+             cap=16, kb=16, vb=16, o=16, lse=None, dbg=None, stream=None)
+    a.update(kw)
+    return m.lib().e2d2_attn_denoise_step_noalloc(*a.values())
+
+
+def test_denoise_noalloc_validation_returns_before_launch():
+    assert _noalloc(q=None) == ERR_NULL
+    assert _noalloc(kc=None) == ERR_NULL
+    assert _noalloc(C=17) == ERR_SHAPE           # cache_len > cache_cap
+    assert _noalloc(Hq=3, Hkv=2) == ERR_SHAPE
+    assert _noalloc(q=24) == ERR_SHAPE           # misaligned
+    assert _noalloc(d=16) == ERR_UNSUPPORTED
+    assert _noalloc(dtype=7) == ERR_UNSUPPORTED
+
+
 def _enc_varlen(**kw):
     a = dict(dtype=m.BF16, B=2, Hq=2, Hkv=1, L=64, d=64, S=8, scale=0.125, q=16, k=16, v=16,
              kv_rows=80, lens=16, o=16, lse=None, dbg=None, stream=None)
