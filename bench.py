@@ -116,7 +116,7 @@ def graph_of(fn, n):
     return g
 
 
-def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True):
+def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True, cold=False):
     import torch
 
     import masked_attention_amd as m
@@ -151,14 +151,69 @@ def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True):
     clock_warmup(g.replay)
     stream = torch.cuda.current_stream(dev)
     t0 = time.perf_counter()
-    total_ms, kern_ms = timed_launches(g.replay, 1, stream)
-    kern_ms = total_ms / steps
+    total_ms, _ = timed_launches(g.replay, 1, stream)
     wall = time.perf_counter() - t0
     if not (torch.equal(od, ref[0]) and torch.equal(oe, ref[1])):
         raise RuntimeError("graph replay differs from the eager launch")
     useful = 4.0 * d * 2 * pairs_blockcausal(L, S) * B * Hq
-    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=kern_ms,
-                useful_flop=useful, wall_s=wall)
+    out = dict(total_ms=total_ms, ms_per_step=total_ms / steps, useful_flop=useful, wall_s=wall)
+    out["kernel_ms"] = per_launch_ms(step, max(8, min(steps, 64)), stream)
+    if cold:
+        out["cold_ms"] = cold_launch_ms(step, 8, stream)
+    return out
+
+
+def per_launch_ms(fn, n, stream):
+    """Median duration of one launch of fn, from HIP events recorded on ``stream`` between
+    consecutive eager launches.  A long replay-free busy loop runs first, so the host
+    enqueues the launches while the GPU is still busy and each event pair brackets the
+    kernel rather than the host's launch path."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    busy = torch.empty(1 << 26, dtype=torch.float32, device=stream.device)
+    clock_warmup(fn)
+    # queued GPU work ahead of the timed launches, longer than the host needs to enqueue
+    # them (~50 us per launch and event on the host)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    busy.mul_(1.0)
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-5)
+    for _ in range(int(3 * n * 50e-6 / one) + 2):
+        busy.mul_(1.0)
+    ev[0].record(stream)
+    for i in range(n):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    return ms[len(ms) // 2]
+
+
+def cold_launch_ms(fn, n, stream):
+    """Median duration of one launch of fn right after a 1 GiB read sweep that leaves
+    the 256 MB Infinity Cache and the L2s holding other, clean lines, so the inputs
+    come from HBM.  The sweep keeps the GPU busy while the host records the start
+    event and launches fn, so the event pair brackets the kernel."""
+    import torch
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=stream.device)
+    clock_warmup(fn)
+    ms = []
+    for _ in range(n):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        flush.sum()
+        start.record(stream)
+        fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms.append(start.elapsed_time(end))
+    del flush
+    ms.sort()
+    return ms[len(ms) // 2]
 
 
 def bench_train_bwd(B, Hq, Hkv, L, S, d, steps, seed):
@@ -492,52 +547,172 @@ def bench_decoder_layer(steps_per_block, reps, seed):
     )
 
 
-def bench_near_ar(steps, seed):
-    """Near-autoregressive decoding: B64 H32 (MHA) d128, a 32768-row cache, block 4.
-    Each step streams the whole cache (34 GB), so it is timed eagerly, step by step."""
+def bench_sampling_block(T, reps, seed):
+    """One block of the sampling loop ("Encoder-Decoder Diffusion Language Models for
+    Efficient Training and Inference", Paper-Notes page, 方法详解 §3 采样算法: T
+    decoder steps against the encoder's KV cache, then the finished block through the
+    encoder, which extends the cache) at the denoise workload's shape, for one encoder
+    layer and one decoder layer in the shared-KV wiring (the decoder layer reads the
+    encoder layer's cache):
+      * T decoder-layer denoising steps (QKV projection, attention over the cache plus
+        the noised block, output projection), fresh hidden states per step;
+      * the encoder layer's update of the finished block: the same attention sublayer
+        on the block's clean hidden states, whose k/v outputs are the block's rows of
+        the cache;
+      * the append of those rows.
+    Each part and the whole block are replayed from HIP graphs and timed with HIP
+    events; the append rewrites the same cache rows on every replay."""
+    import torch
+
+    import masked_attention_amd as m
+    from synth import TensorKind as K, device_draw, device_fill, tensor_id
+
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, C, S = 32, 16, 8, 128, 2048, 32
+    Dm = Hq * d
+    cap = C + S
+    kc = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    device_fill(kc, seed, tensor_id(K.K_CACHE), rows=C)
+    device_fill(vc, seed, tensor_id(K.V_CACHE), rows=C)
+
+    def draw(shape, kind, step=0, block=0, scale=None):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        device_draw(t, seed, tensor_id(kind, step=step, block=block))
+        if scale is not None:
+            t.mul_(scale)  # ~1/sqrt(fan-in), a power of two (exact in bf16)
+        return t
+
+    xs = [draw((B, S, Dm), K.X_BLK, step=t) for t in range(T)]
+    x_clean = draw((B, S, Dm), K.X_BLK, block=1)
+    w = {}
+    for layer, blk in (("dec", 0), ("enc", 1)):
+        w[layer] = (draw(((Hq + 2 * Hkv) * d, Dm), K.W_QKV, block=blk, scale=2.0 ** -6),
+                    draw((Dm, Hq * d), K.W_O, block=blk, scale=2.0 ** -6))
+
+    def act():
+        q = torch.empty((B, Hq, S, d), dtype=torch.bfloat16, device=dev)
+        k = torch.empty((B, Hkv, S, d), dtype=torch.bfloat16, device=dev)
+        return (q, k, torch.empty_like(k), torch.empty_like(q),
+                torch.empty((B, S, Dm), dtype=torch.bfloat16, device=dev),
+                torch.empty((B, Hq, S), device=dev))
+
+    a_dec, a_enc = act(), act()
+    nws = m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, Hq, Hkv, S, d, C)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    it = [0]
+
+    def dec_steps():
+        for t in range(T):
+            q, k, v, o, y, lse = a_dec
+            m.e2d2_decoder_layer_denoise_step(xs[t], *w["dec"], kc, vc, C, q, k, v, o, y,
+                                              lse_blk=lse, workspace=ws)
+
+    def enc_update():
+        q, k, v, o, y, lse = a_enc
+        m.e2d2_decoder_layer_denoise_step(x_clean, *w["enc"], kc, vc, C, q, k, v, o, y,
+                                          lse_blk=lse, workspace=ws)
+        m.e2d2_kv_cache_append(kc, vc, C, k, v)
+
+    def block():
+        dec_steps()
+        enc_update()
+
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, fn in (("block", block), ("decoder_steps", dec_steps), ("encoder_update", enc_update)):
+        g = graph_of(fn, 1)
+        g.replay()
+        clock_warmup(g.replay)
+        ms = sorted(timed_launches(g.replay, 1, stream)[1] for _ in range(reps))
+        res[name] = ms[len(ms) // 2]
+    return dict(
+        workload=f"one sampling-loop block, B32 Hq16 Hkv8 d128 Dm2048, cache 2048, block 32, "
+                 f"bf16: {T} decoder-layer steps + the encoder layer's update of the "
+                 "finished block + the KV-cache append (one encoder and one decoder layer)",
+        us_per_block=round(res["block"] * 1e3, 2),
+        decoder_steps_us=round(res["decoder_steps"] * 1e3, 2),
+        decoder_us_per_step=round(res["decoder_steps"] * 1e3 / T, 2),
+        encoder_update_us=round(res["encoder_update"] * 1e3, 2),
+        encoder_share=round(res["encoder_update"] / res["block"], 4),
+        tokens_per_s_per_layer_pair=round(B * S / (res["block"] * 1e-3), 1),
+    )
+
+
+def bench_near_ar(blocks, steps, seed):
+    """Near-autoregressive decoding: B64 H32 (MHA) d128, block 4, a cache that starts at
+    32768 rows; `blocks` blocks of `steps` denoising steps each, every block followed by
+    the KV-cache append of its 4 rows (cache_len grows by 4 per block), with fresh
+    block tensors for every step.  Each step streams the whole cache (34 GB), so the
+    loop runs eagerly; HIP events bracket every step and append and the whole loop."""
     import torch
 
     import masked_attention_amd as m
     from synth import TensorKind as K, device_fill, tensor_id
 
     dev = torch.device("cuda:0")
-    B, H, d, C, S = 64, 32, 128, 32768, 4
-    cap = C + 16 * S
+    B, H, d, C0, S = 64, 32, 128, 32768, 4
+    cap = C0 + blocks * S
     kc = torch.empty((B, H, cap, d), dtype=torch.bfloat16, device=dev)
     vc = torch.empty_like(kc)
-    device_fill(kc, seed, tensor_id(K.K_CACHE), rows=C)
-    device_fill(vc, seed, tensor_id(K.V_CACHE), rows=C)
+    device_fill(kc, seed, tensor_id(K.K_CACHE), rows=C0)
+    device_fill(vc, seed, tensor_id(K.V_CACHE), rows=C0)
 
-    def fill(kind, t):
+    def fill(kind, t, k):
         x = torch.empty((B, H, S, d), dtype=torch.bfloat16, device=dev)
-        device_fill(x, seed, tensor_id(kind, step=t))
+        device_fill(x, seed, tensor_id(kind, step=t, block=k))
         return x
 
-    qs = [fill(K.Q_BLK, t) for t in range(steps)]
-    ks = [fill(K.K_BLK, t) for t in range(steps)]
-    vs = [fill(K.V_BLK, t) for t in range(steps)]
-    kn, vn = fill(K.K_NEW, 0), fill(K.V_NEW, 0)
+    blk = [[(fill(K.Q_BLK, t, k), fill(K.K_BLK, t, k), fill(K.V_BLK, t, k)) for t in range(steps)]
+           for k in range(blocks)]
+    new = [(fill(K.K_NEW, 0, k), fill(K.V_NEW, 0, k)) for k in range(blocks)]
     o = torch.empty((B, H, S, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, S), device=dev)
-    assert m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, H, H, S, d, C) == 0
+    assert m.e2d2_attn_denoise_workspace_bytes(m.BF16, B, H, H, S, d, C0) == 0
     stream = torch.cuda.current_stream(dev)
 
-    def step(t):
-        m.e2d2_attn_denoise_step(qs[t], kc, vc, C, ks[t], vs[t], o, lse_blk=lse)
+    def step(k, t):
+        q, kb, vb = blk[k][t]
+        m.e2d2_attn_denoise_step(q, kc, vc, C0 + k * S, kb, vb, o, lse_blk=lse)
 
-    for t in range(steps):  # warm-up (each step is several ms of sustained streaming)
-        step(t)
-    ms = []
-    for t in range(steps):
-        _, one = timed_launches(lambda: step(t), 1, stream)
-        ms.append(one)
-    _, app = timed_launches(lambda: m.e2d2_kv_cache_append(kc, vc, C, kn, vn), 1, stream)
-    alg = 2 * B * H * C * d * 2 + 2 * B * H * S * d * 2 + B * H * S * d * 2 + B * H * S * d * 2 + B * H * S * 4
-    med = sorted(ms)[len(ms) // 2]
-    return dict(workload="near-AR denoise step, B64 H32 (MHA) d128 cache 32768 block 4, bf16",
-                ms_per_step=med, steps_timed=len(ms), algorithmic_bytes_per_step=alg,
-                gbs=alg / (med * 1e-3) / 1e9, frac_of_hbm_peak=alg / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                append_us=app * 1e3)
+    for t in range(steps):  # warm-up at the first length (each step is ms of streaming)
+        step(0, t)
+    torch.cuda.synchronize()
+    ev = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(blocks):
+        for t in range(steps):
+            step(k, t)
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev.append(("step", e))
+        m.e2d2_kv_cache_append(kc, vc, C0 + k * S, *new[k])
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.append(("append", e))
+    torch.cuda.synchronize()
+    step_ms, app_ms = [], []
+    prev = e0
+    for kind, e in ev:
+        (step_ms if kind == "step" else app_ms).append(prev.elapsed_time(e))
+        prev = e
+    total = e0.elapsed_time(ev[-1][1])
+    alg = 0  # algorithmic bytes of every step: the cache rows read, own K/V, Q, O, LSE
+    for k in range(blocks):
+        C = C0 + k * S
+        alg += steps * (2 * B * H * C * d * 2 + 2 * B * H * S * d * 2 + 2 * B * H * S * d * 2
+                        + B * H * S * 4)
+    app_bytes = blocks * 2 * 2 * B * H * S * d * 2
+    med = sorted(step_ms)[len(step_ms) // 2]
+    gbs = alg / (sum(step_ms) * 1e-3) / 1e9
+    return dict(workload=f"near-AR decoding, B64 H32 (MHA) d128, cache 32768 + 4 per block, block 4, "
+                         f"{blocks} blocks x {steps} steps with an append after each block, bf16",
+                total_ms=round(total, 2), steps_timed=len(step_ms),
+                ms_per_step_mean=round(sum(step_ms) / len(step_ms), 4), ms_per_step_median=round(med, 4),
+                append_us_mean=round(sum(app_ms) / len(app_ms) * 1e3, 2),
+                algorithmic_bytes=alg, gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4),
+                total_with_appends_gbs=round((alg + app_bytes) / (total * 1e-3) / 1e9, 1))
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -574,13 +749,76 @@ def cpu_baseline(budget_s: float = 12.0):
                 seconds=round(t_total, 2), host_cpus=os.cpu_count())
 
 
+def _time_repeat(fn, min_s):
+    """Run fn until at least min_s seconds have passed; returns (calls, seconds)."""
+    n, t = 0, 0.0
+    while t < min_s:
+        t0 = time.perf_counter()
+        fn()
+        t += time.perf_counter() - t0
+        n += 1
+    return n, t
+
+
+def cpu_baseline_other(min_s: float = 3.0):
+    """The fp64 oracle on the other workloads, each timed on a slice (the oracle's cost
+    depends only on the shapes, so a slice's time scales to the whole workload; every
+    figure that is scaled says so):
+      * denoise step B32 Hq16 Hkv8 d128 C2048 S32: the 16 query heads of one sequence,
+        scaled to 32 sequences;
+      * long training forward B2 Hq16 Hkv8 d128 L8192 S64: one query head, encoder and
+        decoder, scaled to 32 heads;
+      * near-AR step B64 H32 d128 C32768 S4: one head, scaled to 2048 heads per step and
+        to the 64 steps of 16 blocks x 4 (cache 32768 + 4 per block)."""
+    import oracle
+    from synth import TensorKind as K, host_tensor, tensor_id
+
+    out = []
+    # denoise step
+    seed, B, Hq, Hkv, d, C, S = 0xE2D20003, 32, 16, 8, 128, 2048, 32
+    g = lambda kind, shape, **kw: host_tensor(seed, tensor_id(kind), shape, "bf16", **kw)
+    q = g(K.Q_BLK, (1, Hq, S, d))
+    kc, vc = g(K.K_CACHE, (1, Hkv, C, d)), g(K.V_CACHE, (1, Hkv, C, d))
+    kb, vb = g(K.K_BLK, (1, Hkv, S, d)), g(K.V_BLK, (1, Hkv, S, d))
+    n, t = _time_repeat(lambda: oracle.denoise_step(q, kc, vc, C, kb, vb, 1 / math.sqrt(d)), min_s)
+    per_step = t / n * B
+    out.append(dict(workload="denoise step, B32 Hq16 Hkv8 d128 cache 2048 block 32", kind="oracle",
+                    value=round(per_step * 1e6, 1), unit="us per step (extrapolated)",
+                    sample=f"16 query heads of 1 of 32 sequences, {n} calls in {t:.2f} s, x 32"))
+    # long training forward
+    seed, L, S, d = 0xE2D20004, 8192, 64, 128
+    g = lambda kind: host_tensor(seed, tensor_id(kind), (1, 1, L, d), "bf16")
+    qd, qe, kc, vc, kd, vd = (g(k) for k in (K.Q_DEC, K.Q_ENC, K.K_CTX, K.V_CTX, K.K_DEC, K.V_DEC))
+    t0 = time.perf_counter()
+    oracle.train_fwd(qd, kc, vc, kd, vd, S, 1 / math.sqrt(d), q_enc=qe)
+    t = time.perf_counter() - t0
+    useful = 4.0 * d * 2 * pairs_blockcausal(L, S)
+    out.append(dict(workload="long training forward, B2 Hq16 Hkv8 d128 L8192 S64, encoder + decoder",
+                    kind="oracle", value=round(useful / t / 1e12, 5), unit="TFLOP/s",
+                    seconds_per_head=round(t, 2), seconds_whole=round(t * 32, 1),
+                    sample="1 of 32 query heads (both masks); seconds_whole = x 32 (extrapolated)"))
+    # near-AR step
+    seed, d, C0, S = 0xE2D20005, 128, 32768, 4
+    g = lambda kind, n: host_tensor(seed, tensor_id(kind), (1, 1, n, d), "bf16")
+    q, kb, vb = g(K.Q_BLK, S), g(K.K_BLK, S), g(K.V_BLK, S)
+    kc, vc = g(K.K_CACHE, C0), g(K.V_CACHE, C0)
+    n, t = _time_repeat(lambda: oracle.denoise_step(q, kc, vc, C0, kb, vb, 1 / math.sqrt(d)), min_s)
+    per_step = t / n * 64 * 32
+    out.append(dict(workload="near-AR step, B64 H32 d128 cache 32768 block 4", kind="oracle",
+                    value=round(per_step * 1e3, 1), unit="ms per step (extrapolated)",
+                    seconds_64_steps=round(per_step * 64, 1),
+                    sample=f"1 of 2048 heads at cache 32768, {n} calls in {t:.2f} s, x 2048 heads; "
+                           "x 64 steps for the 16 blocks x 4 (extrapolated)"))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", choices=["all", "train", "bwd", "layers", "denoise", "long", "nearar",
-                                       "declayer", "copycal"],
+                                       "declayer", "sampling", "copycal"],
                     default="all",
                     help="restrict the run (profiling); 'copycal' runs only a plain 1 GiB "
                          "device copy, the reference for scaling HBM byte counters")
@@ -611,7 +849,7 @@ def main():
         return
     if args.only in ("all", "train"):
         B, H, L, S, d = 8, 16, 1024, 16, 64
-        train = bench_train(B, H, H, L, S, d, args.steps, args.warmup, 0xE2D20002)
+        train = bench_train(B, H, H, L, S, d, args.steps, args.warmup, 0xE2D20002, cold=True)
         print(f"[bench] train fwd B{B} H{H} d{d} L{L} S{S}: {train['ms_per_step'] * 1e3:.1f} us/step, "
               f"kernel {train['kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
     if args.only in ("all", "bwd"):
@@ -642,14 +880,19 @@ def main():
         print(f"[bench] denoise varlen: {out['denoise_varlen']['us_per_step_warm']:.1f} us "
               f"({out['denoise_varlen']['gbs_warm']:.0f} GB/s)", file=sys.stderr, flush=True)
 
+    if args.only in ("all", "sampling"):
+        out["sampling_block"] = bench_sampling_block(32, 5, 0xE2D20003)
+        print(f"[bench] sampling block: {out['sampling_block']}", file=sys.stderr, flush=True)
+
     if args.only in ("all", "declayer"):
         out["decoder_layer"] = bench_decoder_layer(32, 5, 0xE2D20003)
         print(f"[bench] decoder layer step: {out['decoder_layer']}", file=sys.stderr, flush=True)
 
     if args.only in ("all", "nearar"):
-        out["near_ar"] = bench_near_ar(8, 0xE2D20005)
-        print(f"[bench] near-AR: {out['near_ar']['ms_per_step']:.3f} ms/step "
-              f"({out['near_ar']['gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+        out["near_ar"] = bench_near_ar(16, 4, 0xE2D20005)
+        print(f"[bench] near-AR: {out['near_ar']['total_ms']:.1f} ms for 64 steps, "
+              f"{out['near_ar']['ms_per_step_mean']:.3f} ms/step ({out['near_ar']['gbs']:.0f} GB/s)",
+              file=sys.stderr, flush=True)
 
     if train is None:
         print(json.dumps(out))
@@ -692,10 +935,17 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "flop_per_byte": round(train["useful_flop"] / alg_bytes, 1),
                      "hbm_roof_tflops": round(train["useful_flop"] / alg_bytes * PEAK_HBM_GBS / 1e3, 1)},
+        "train_cold": {"us": round(train["cold_ms"] * 1e3, 2),
+                       "tflops": round(train["useful_flop"] / (train["cold_ms"] * 1e-3) / 1e12, 1),
+                       "hbm_gbs": round(alg_bytes / (train["cold_ms"] * 1e-3) / 1e9, 1),
+                       "note": "one launch right after a 1 GiB read sweep (inputs from HBM); "
+                               "value and roofline are the warm figures (inputs in the "
+                               "Infinity Cache after the previous launch)"},
     }
     line.update(out)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline_other"] = cpu_baseline_other()
     print(json.dumps(line))
 
 

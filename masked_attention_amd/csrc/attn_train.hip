@@ -384,7 +384,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
   float o[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) o[j] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  // Running max in base-2 units (max score times c) and the sum relative to it.  The
+  // rescale factor is 2^(old - new) of two stored values, so it is exactly 1 whenever
+  // the max did not change (recomputing old * c there could leave a rounding residue
+  // that would reweight earlier keys against later ones at every sub-block).
+  float mb = -INFINITY, l = 0.f;
   const float c = p.c;
   int visits = 0;
 
@@ -406,32 +410,40 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
         vs[r][col] = vb[(size_t)g * D + col];
       }
       __syncthreads();
+      // Rounding error is kept well under 1e-5 relative at thousands of keys: four
+      // partial sums per dot product, and the 16 keys of a sub-block are summed on
+      // their own before one fused multiply-add folds them into the running O and l.
       for (int sub = 0; sub < BN; sub += 16) {
         float s[16];
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * BN + sub + r;
-          float acc = 0.f;
+          float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < D; ++j) acc = fmaf(q[j], ks[sub + r][j], acc);
+          for (int j = 0; j < D; ++j) a[j & 3] = fmaf(q[j], ks[sub + r][j], a[j & 3]);
+          const float acc = (a[0] + a[1]) + (a[2] + a[3]);
           s[r] = (key >= iv.lo && key < iv.hi) ? acc : -INFINITY;
           mx = fmaxf(mx, s[r]);
         }
-        const float m_new = fmaxf(m, mx);
-        const float base = m_new == -INFINITY ? 0.f : m_new * c;
-        const float alpha = exp2f(m * c - base);
-        l *= alpha;
-#pragma unroll
-        for (int j = 0; j < D; ++j) o[j] *= alpha;
+        const float mb_new = fmaxf(mb, mx * c);
+        const float base = mb_new == -INFINITY ? 0.f : mb_new;
+        const float alpha = exp2f(mb - base);
+        float ls = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2f(fmaf(s[r], c, -base));
-          l += e;
-#pragma unroll
-          for (int j = 0; j < D; ++j) o[j] = fmaf(e, vs[sub + r][j], o[j]);
+          s[r] = exp2f(fmaf(s[r], c, -base));  // the numerator, in place
+          ls += s[r];
         }
-        m = m_new;
+        l = fmaf(l, alpha, ls);
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          float part = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part = fmaf(s[r], vs[sub + r][j], part);
+          o[j] = fmaf(o[j], alpha, part);
+        }
+        mb = mb_new;
       }
     }
   }
@@ -440,7 +452,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
     const float inv = 1.f / l;
 #pragma unroll
     for (int j = 0; j < D; ++j) orow[j] = o[j] * inv;
-    if (p.lse[slot] != nullptr) p.lse[slot][((size_t)b * p.Hq + hq) * Lq + qi] = m * p.scale + logf(l);
+    if (p.lse[slot] != nullptr)
+      p.lse[slot][((size_t)b * p.Hq + hq) * Lq + qi] = mb * 0.6931471805599453f + logf(l);
   }
   if (p.visits != nullptr && lane == 0) atomicAdd(p.visits, (unsigned long long)visits);
 }
