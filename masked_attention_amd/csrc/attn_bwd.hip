@@ -56,11 +56,23 @@ __global__ __launch_bounds__(256, D > 64 ? 2 : 3) void bwd_dq_kernel(BwdParams p
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
 
-  // work item, as in the forward: query tiles from the last to the first
+  // work item, as in the forward: query tiles from the last to the first; when the
+  // items of a tile level split evenly over the 8 XCDs (workgroups are dealt to them
+  // round-robin), each XCD keeps a fixed contiguous set of heads, so a head's K/V tiles
+  // are fetched into one XCD's L2 only
   const int BH = p.B * p.Hq;
   const int per_level = BH * p.n_kinds;
-  const int level = blockIdx.x / per_level;
-  const int rem = blockIdx.x % per_level;
+  const int w = blockIdx.x;
+  int level, rem;
+  if ((per_level & 7) == 0) {
+    const int per_xcd = per_level >> 3;
+    const int local = w >> 3;
+    level = local / per_xcd;
+    rem = (w & 7) * per_xcd + local % per_xcd;
+  } else {
+    level = w / per_level;
+    rem = w % per_level;
+  }
   const int slot = rem % p.n_kinds;
   const int bh = rem / p.n_kinds;
   const int kind = slot ? p.kinds[1] : p.kinds[0];
@@ -287,9 +299,20 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
 
   // work item: (level, b, hk); levels 0..n_ktiles-1 are the clean keys' tiles in
   // increasing key order (most queries first), then the noised keys' tiles
+  // (batch, kv head) units grouped per XCD as in the dQ kernel: the key tiles of a unit,
+  // which all stream the same Q / dO tiles, share one XCD's L2
   const int BK = p.B * p.Hkv;
-  const int level = blockIdx.x / BK;
-  const int bk = blockIdx.x % BK;
+  const int w = blockIdx.x;
+  int level, bk;
+  if ((BK & 7) == 0) {
+    const int per_xcd = BK >> 3;
+    const int local = w >> 3;
+    level = local / per_xcd;
+    bk = (w & 7) * per_xcd + local % per_xcd;
+  } else {
+    level = w / BK;
+    bk = w % BK;
+  }
   const int b = bk / p.Hkv, hk = bk % p.Hkv;
   const int src = level < p.n_ktiles ? 0 : 1;
   const int k0 = (src ? level - p.n_ktiles : level) * kRows;
