@@ -156,64 +156,42 @@ def bench_train(B, Hq, Hkv, L, S, d, steps, warmup, seed, with_lse=True, cold=Fa
     if not (torch.equal(od, ref[0]) and torch.equal(oe, ref[1])):
         raise RuntimeError("graph replay differs from the eager launch")
     useful = 4.0 * d * 2 * pairs_blockcausal(L, S) * B * Hq
-    out = dict(total_ms=total_ms, ms_per_step=total_ms / steps, useful_flop=useful, wall_s=wall)
-    out["kernel_ms"] = per_launch_ms(step, max(8, min(steps, 64)), stream)
+    # kernel_ms: the mean launch duration over the timed region (the launches run back to
+    # back from the graph; the kernel trace's per-dispatch average agrees)
+    out = dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=total_ms / steps,
+               useful_flop=useful, wall_s=wall)
     if cold:
-        out["cold_ms"] = cold_launch_ms(step, 8, stream)
+        out["cold_ms"] = cold_launch_ms(step, 9, stream)
     return out
 
 
-def per_launch_ms(fn, n, stream):
-    """Median duration of one launch of fn, from HIP events recorded on ``stream`` between
-    consecutive eager launches.  A long replay-free busy loop runs first, so the host
-    enqueues the launches while the GPU is still busy and each event pair brackets the
-    kernel rather than the host's launch path."""
-    import torch
-
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-    busy = torch.empty(1 << 26, dtype=torch.float32, device=stream.device)
-    clock_warmup(fn)
-    # queued GPU work ahead of the timed launches, longer than the host needs to enqueue
-    # them (~50 us per launch and event on the host)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    busy.mul_(1.0)
-    torch.cuda.synchronize()
-    one = max(time.perf_counter() - t0, 1e-5)
-    for _ in range(int(3 * n * 50e-6 / one) + 2):
-        busy.mul_(1.0)
-    ev[0].record(stream)
-    for i in range(n):
-        fn()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
-    return ms[len(ms) // 2]
-
-
 def cold_launch_ms(fn, n, stream):
-    """Median duration of one launch of fn right after a 1 GiB read sweep that leaves
-    the 256 MB Infinity Cache and the L2s holding other, clean lines, so the inputs
-    come from HBM.  The sweep keeps the GPU busy while the host records the start
-    event and launches fn, so the event pair brackets the kernel."""
+    """Duration of one launch of fn with its inputs in HBM: the median time of a read
+    sweep over 1 GiB (which leaves the 256 MB Infinity Cache and the L2s holding other,
+    clean lines) followed by fn, minus the median time of the sweep alone, each timed as
+    one region between HIP events on ``stream``.  No event sits between the sweep and fn,
+    so the difference holds the kernel and not an event's dispatch gap."""
     import torch
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device=stream.device)
     clock_warmup(fn)
-    ms = []
-    for _ in range(n):
+
+    def region(with_fn):
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        flush.sum()
         start.record(stream)
-        fn()
+        flush.sum()
+        if with_fn:
+            fn()
         end.record(stream)
         torch.cuda.synchronize()
-        ms.append(start.elapsed_time(end))
+        return start.elapsed_time(end)
+
+    both = sorted(region(True) for _ in range(n))
+    sweep = sorted(region(False) for _ in range(n))
     del flush
-    ms.sort()
-    return ms[len(ms) // 2]
+    return both[n // 2] - sweep[n // 2]
 
 
 def bench_train_bwd(B, Hq, Hkv, L, S, d, steps, seed):
@@ -427,33 +405,22 @@ def bench_denoise(steps_per_block, blocks, warm_blocks, seed):
         end.record(stream)
         torch.cuda.synchronize()
         append_ms.append(start.elapsed_time(end))
-    # cold: before each step, sweep a 1 GiB buffer with reads only, so the 256 MB
-    # Infinity Cache and the L2 hold other, clean lines (a write sweep would leave dirty
-    # lines whose write-back would be charged to the step)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    clock_warmup(g.replay)
-    # The flush keeps the GPU busy for a few hundred us, far longer than the host needs to
-    # record the start event and launch the step, so the step starts right after the
-    # event and the pair times the kernel, not the launch path of one isolated call.
-    cold_ms = []
-    for t in range(min(T, 16)):
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        flush.sum()
-        start.record(stream)
-        step(t)
-        end.record(stream)
-        torch.cuda.synchronize()
-        cold_ms.append(start.elapsed_time(end))
-    del flush
+    # cold: each step with its inputs in HBM (cold_launch_ms: a 1 GiB read sweep, which
+    # leaves the 256 MB Infinity Cache and the L2s holding other, clean lines, then the
+    # step, minus the sweep alone)
+    it_cold = [0]
+
+    def cold_step():
+        step(it_cold[0] % T)
+        it_cold[0] += 1
+
+    cold = cold_launch_ms(cold_step, 9, stream)
     cache_bytes = 2 * B * Hkv * C * d * 2
     blk_bytes = 2 * B * Hkv * S * d * 2
     q_bytes = B * Hq * S * d * 2
     o_bytes = B * Hq * S * d * 2 + B * Hq * S * 4
     alg = cache_bytes + blk_bytes + q_bytes + o_bytes
     warm = sorted(step_ms)[len(step_ms) // 2]
-    cold = sorted(cold_ms)[len(cold_ms) // 2]
     app = sorted(append_ms)[len(append_ms) // 2]
     app_bytes = 2 * 2 * B * Hkv * S * d * 2
     return dict(
