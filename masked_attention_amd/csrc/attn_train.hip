@@ -220,7 +220,9 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   float l = 0.f;       // lane-partial running sum, relative to ms
   const float c = p.c;
 
-  // Element mask of the partly allowed blocks of tile t.
+  // Element mask of the partly allowed blocks of tile t.  The lane's 16 keys are
+  // kr + {0..3, 8..11, 16..19, 24..27}; bit k of `bits` says whether key kr + k is
+  // allowed, so each score takes one bit extract and one bit select.
   auto mask = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
     const int src = tsrc(t);
     const int kt0 = tnum(t) * kBN;
@@ -228,10 +230,15 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     for (int kb = 0; kb < 2; ++kb) {
       if (cls[kb] == 1) {
         const int kr = kt0 + kb * 32 + ((lane >> 5) << 2);
+        const int a = min(max(iv[src].lo - kr, 0), 32);
+        const int e = min(max(iv[src].hi - kr, 0), 32);
+        const uint32_t bits =
+            e <= a ? 0u : (e - a >= 32 ? 0xffffffffu : ((1u << (e - a)) - 1u) << a);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = kr + ((j >> 2) << 3) + (j & 3);
-          if (key < iv[src].lo || key >= iv[src].hi) sc[kb][j] = -INFINITY;
+          const int off = ((j >> 2) << 3) + (j & 3);
+          const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - off)) >> 31);
+          sc[kb][j] = __uint_as_float((__float_as_uint(sc[kb][j]) & keep) | (~keep & 0xff800000u));
         }
       }
     }
@@ -243,7 +250,20 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   // rescales O and l, and the block's numerators are formed again.  The decision is
   // per row (the lane pair), so a row's arithmetic depends on its own keys only.  Each
   // block's P^T is accumulated right after its numerators, so one block's P is live.
+  // The wave's first block starts from O = 0 and l = 0: each row takes its max over
+  // the block at once (rows with no allowed key there keep the "no key yet" max).
+  bool started = false;  // wave-uniform
   auto block_softmax = [&](const f32x16& sblk, bf16x8 (&pbk)[2]) {
+    if (!started) {
+      started = true;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sblk[j]);
+      const float rmax = pair_max(mx);
+      if (rmax > -INFINITY) ms = rmax * c;
+      l = exp_pack(sblk, c, -ms, pbk, 0.f);
+      return;
+    }
     float rs = exp_pack(sblk, c, -ms, pbk, 0.f);
     if (__builtin_amdgcn_ballot_w64(rs > kBound) != 0) {
       float mx = -INFINITY;
