@@ -66,9 +66,32 @@ def check(got, ref, dtype, what=""):
     return float(rel.max())
 
 
+def check_scaled(got, ref, what="", rel=2e-2):
+    """Element-wise check for quantities whose rounding error scales with their row:
+    |got - ref| <= rel * max(|ref|, rms of ref's row (last axis), 1e-3 * rms of ref).
+    The row floor covers elements that a sum cancels to near zero, whose error still
+    follows the size of the terms; the last floor covers rows that are zero in exact
+    arithmetic (a query with one allowed key has dS = 0) and come out as rounding
+    residue.  Returns the max scaled error."""
+    g = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - r)
+    rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    floor = max(1e-3 * float(np.sqrt(np.mean(r * r))), 1e-30)
+    scaled = err / np.maximum(np.maximum(np.abs(r), rms), floor)
+    bad = scaled > rel
+    if bad.any():
+        idx = np.unravel_index(np.argmax(scaled), scaled.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements beyond {rel} x max(|ref|, row rms); "
+                             f"max {scaled.max():.3e} at {idx} (got {g[idx]}, ref {r[idx]})")
+    return float(scaled.max())
+
+
 def scale_of(d):
     return 1.0 / math.sqrt(d)
 
 
-__all__ = ["TensorKind", "host", "on_gpu", "gpu_fill", "counter", "check", "scale_of",
+__all__ = ["TensorKind", "host", "on_gpu", "gpu_fill", "counter", "check", "check_scaled", "scale_of",
            "BF16_ATOL", "F32_RTOL", "TORCH_DT"]

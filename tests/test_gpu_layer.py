@@ -8,8 +8,11 @@ Tolerances, element-wise:
     GPU's fp32 sum sits within a tiny fraction of a spacing of the exact one, so they
     differ by at most one step where the exact value is near a rounding midpoint.
   * o, lse: the attention's bf16 bar, |d| <= 2e-2.
-  * y: |d| <= 2e-2 * max |y_ref|.  y is linear in o; o carries the attention's
-    relative error (bf16 P and O, ~2^-8 each) and y's own bf16 rounding adds 2^-9.
+  * y: |d| <= 2e-2 * max(|y_ref|, rms of y_ref's row over the model width), element by
+    element.  y is a sum over the heads' o (bf16, ~2^-8 relative from bf16 P and O)
+    times bf16 weights, accumulated in fp32, plus y's own bf16 rounding (2^-9): its
+    error follows the size of its terms, with the row's RMS as the floor for elements
+    the sum cancels to near zero.
 """
 import math
 import sys
@@ -20,7 +23,7 @@ import torch
 
 import masked_attention_amd as m
 import oracle
-from helpers import TensorKind as K, check, gpu_fill, host, scale_of
+from helpers import TensorKind as K, check, check_scaled, gpu_fill, host, scale_of
 from synth import device_draw, host_draw, tensor_id
 
 pytestmark = pytest.mark.gpu
@@ -72,16 +75,7 @@ def check_bf16_step(got, ref, what):
 
 
 def check_rel(got, ref, what, rel=2e-2):
-    g = got.detach().double().cpu().numpy()
-    r = np.asarray(ref, dtype=np.float64)
-    assert g.shape == r.shape, (what, g.shape, r.shape)
-    assert np.isfinite(g).all(), f"{what}: non-finite"
-    tol = rel * float(np.abs(r).max())
-    err = np.abs(g - r)
-    if (err > tol).any():
-        idx = np.unravel_index(np.argmax(err), err.shape)
-        raise AssertionError(f"{what}: {int((err > tol).sum())} elements beyond {tol:.3g}; max "
-                             f"err {err.max():.3e} at {idx} (got {g[idx]}, ref {r[idx]})")
+    check_scaled(got, ref, what, rel)
 
 
 @pytest.mark.parametrize("B,S,Dm,Hq,Hkv,d,C", [
