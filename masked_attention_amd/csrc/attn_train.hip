@@ -16,18 +16,26 @@
 //     HBM straight into a 2-deep ring of swizzled LDS stages (buffer_load ... lds);
 //     tile t+1 is in flight while tile t is computed, and other workgroups on the CU
 //     (4 at d <= 64, 2 at d = 128) fill the gaps.
-//   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so a
-//     lane holds 16 keys of ONE query row: row reductions are in-lane plus, when
-//     needed, one exchange with lane l^32.
+//   * Scores are formed transposed, S^T = K Q^T, per 32-key x 32-query block as four
+//     16x16 tiles of v_mfma_f32_16x16x32_bf16 (measured on MI355X: 1.94 against 1.58
+//     PFLOP/s for v_mfma_f32_32x32x16_bf16 with random bf16 operands at full load, and
+//     half as long accumulator chains).  Lane l (c = l % 16, g = l / 16) holds, for the
+//     query rows wq0 + c and wq0 + 16 + c, the keys 4g + r and 16 + 4g + r (r < 4) of
+//     the block; a row's 32 keys sit in the four lanes c + 16 g, and its reductions
+//     (only when rescaling and at the end) are two lane swaps.
 //   * Online softmax in base 2 with the scale folded in (p = 2^(s*c - m), c =
 //     scale*log2 e), p packed to bf16 and summed with v_dot2 (the denominator adds the
 //     same rounded values the PV MFMA multiplies).  Rescaling is lazy: a row keeps its
 //     running max until a lane's block sum of p exceeds 2^16, then takes the block's
 //     max (the same softmax; p stays far inside bf16 and fp32 range).  The decision is
-//     per row, so a row's arithmetic depends on its own keys only.
-//   * O^T += V^T P^T per 32-key block, V^T from the transposing LDS read.
+//     per row, so a row's arithmetic depends on its own keys only.  A wave's first
+//     block takes each row's max directly.
+//   * O^T += V^T P^T per 32-key block on 16x16 tiles of head dims x queries: the B
+//     operand is the lane's own 8 numerators, the A operand V^T comes from two
+//     transposing LDS reads (keys 4g .. 4g+3 and 16+4g .. 16+4g+3, the same order).
 //   * Within a tile, each wave classifies its 32x32 key blocks: empty blocks are
-//     skipped (no MFMA), full blocks skip the mask, the rest mask per element.
+//     skipped (no MFMA), full blocks skip the mask, the rest mask per element (one bit
+//     extract and one bit select per score from a per-lane key mask).
 //   * Epilogue: O = O^T / l in bf16, LSE = (m + log2 l) ln 2 in fp32.
 //   * Work order: query tiles are issued from the last (most keys) to the first;
 //     when the number of (head, kind) items per tile level is a multiple of 8, each of
@@ -65,12 +73,36 @@ struct LoopCfg {
 
 template <int D>
 struct Geo {
-  static constexpr int NC = D / 16;   // MFMA k-steps over the head dim for S^T
-  static constexpr int NDB = D / 32;  // 32-wide head-dim blocks of O^T
   static constexpr int TILE = kBN * D;  // bf16 elements of one K or V tile
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int NIW = 2 * (kBN * (D / 8) / 64) / LoopCfg<D>::kWaves;  // loads per wave per tile
 };
+
+// ---------------------------------------------------------------------------------
+// Per wave and 32x32 key-query block (layouts checked on gfx950):
+//   S^T tile (kh, qh) = K[kh*16 .. +16] Q[qh*16 .. +16]^T: A = K rows (lane: key c,
+//     dims 8g .. 8g+7 of each 32-dim step), B = Q^T (lane: query c, the same dims);
+//     C: lane l, register r = S^T[kh*16 + 4g + r][qh*16 + c].
+//   O^T tile (dt, qh) += V^T[dt*16 .. +16][keys] P^T[keys][qh*16 .. +16] over the
+//     block's 32 keys in the lane order 4g + r, 16 + 4g + r: B = the lane's 8
+//     numerators of row qh*16 + c, A = V^T (lane: dim dt*16 + c, the same 8 keys).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// max / sum over the four lanes c + 16 g of one query row (v_permlane32_swap, then
+// v_permlane16_swap: every lane gets its group's values in lane order, checked on gfx950)
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 template <int D>
 __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) void train_fwd_bf16_kernel(TrainParams p) {
@@ -78,14 +110,17 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   constexpr int kStages = LoopCfg<D>::kStages;
   constexpr int kBM = LoopCfg<D>::kBM;
   constexpr int kWaves = LoopCfg<D>::kWaves;
-  constexpr int NC = G::NC, NDB = G::NDB, TILE = G::TILE, STAGE = G::STAGE, NIW = G::NIW;
+  constexpr int TILE = G::TILE, STAGE = G::STAGE;
+  constexpr int NK = D / 32;   // 32-dim k-steps of S^T
+  constexpr int NDT = D / 16;  // 16-dim tiles of O^T
+  static_assert(kStages == 2, "two-stage ring");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
 
-  // ---- work item: query tiles from the last (most keys) to the first; heads grouped
-  //      per XCD when the item count of a tile level is a multiple of 8
+  // ---- work item (as in train_fwd_bf16_kernel)
   const int BH = p.B * p.Hq;
   const int per_level = BH * p.n_kinds;
   const int w = blockIdx.x;
@@ -107,12 +142,10 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   const int hq = bh % p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
   const int S = p.S;
-  // this sequence's length: all L rows, or (per-sequence lengths on the device) its own
-  // prefix of them; the row stride of q, o and lse stays p.L
   const int L = p.lens != nullptr ? min(max(p.lens[b], 0), p.L) : p.L;
 
   const int q0 = qtile * kBM;
-  if (q0 >= L) return;  // the whole query tile lies past this sequence's end
+  if (q0 >= L) return;
   const int r_last = min(q0 + kBM, L) - 1;
   const int nsrc = num_sources(kind);
   const TileRange tr0 = visited_tiles(kind, 0, q0, r_last, S, L, 0, kBN);
@@ -130,7 +163,6 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
   loader.init(wave, lane);
   char E2D2_LDS* lds_b = (char E2D2_LDS*)smem_raw;
 
-  // tile index -> (source, key-tile number in that source)
   auto tsrc = [&](int t) { return t < n0 ? 0 : 1; };
   auto tnum = [&](int t) { return t < n0 ? tr0.first + t : tr1.first + (t - n0); };
   auto issue = [&](int t) {
@@ -144,28 +176,25 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
       loader.load(rv1, row0, kt + TILE * 2, wave);
     }
   };
+  if (0 < ntot) issue(0);
 
-  // first tiles in flight before the per-row setup below
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (i < ntot) issue(i);
-
-  // ---- per-wave rows and per-lane query row
+  // ---- per-wave rows; the lane's two query rows qr[0] = wq0 + c, qr[1] = wq0 + 16 + c
   const int wq0 = q0 + wave * 32;
   const bool wave_live = wq0 < L;
   const int wr1 = min(wq0 + 32, L) - 1;
-  const int qi = wq0 + (lane & 31);
-  const bool row_ok = qi < L;
-  Interval iv[2];
+  int qr[2];
+  bool rok[2];
+  Interval iv[2][2];
 #pragma unroll
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    iv[sidx] = row_interval(kind, sidx, row_ok ? qi : 0, S, L, 0);
-    if (!row_ok) iv[sidx] = Interval{0, 0};
+  for (int qh = 0; qh < 2; ++qh) {
+    qr[qh] = wq0 + qh * 16 + c16;
+    rok[qh] = qr[qh] < L;
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      iv[qh][sidx] = row_interval(kind, sidx, rok[qh] ? qr[qh] : 0, S, L, 0);
+      if (!rok[qh]) iv[qh][sidx] = Interval{0, 0};
+    }
   }
-  // Classification of the two 32-key blocks of tile t for this wave:
-  // 0 = no allowed pair (skipped), 1 = partly allowed (masked), 2 = all allowed.
-  // The keys the wave's rows allow at all (union) and allow in every row (common) are
-  // fixed per source, so a block is classified with four compares.
   Interval wu[2] = {{0, 0}, {0, 0}}, wc[2] = {{0, 0}, {0, 0}};
   if (wave_live) {
 #pragma unroll
@@ -193,179 +222,223 @@ __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) voi
     }
   };
 
+  // queries: qf[qh][kk] = Q[qr[qh]][kk*32 + 8g .. +7]
   const size_t q_off = ((size_t)b * p.Hq + hq) * (size_t)p.L * D;
-  bf16x8 qf[NC];
-  {
-    const __bf16* qrow = p.q[slot] + q_off + (size_t)(row_ok ? qi : 0) * D + ((lane >> 5) << 3);
+  bf16x8 qf[2][NK];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      bf16x8 v = *(const bf16x8*)(qrow + cc * 16);
-      if (!row_ok) {
+  for (int qh = 0; qh < 2; ++qh) {
+    const __bf16* qrow = p.q[slot] + q_off + (size_t)(rok[qh] ? qr[qh] : 0) * D + (g4 << 3);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      bf16x8 v = *(const bf16x8*)(qrow + kk * 32);
+      if (!rok[qh]) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (__bf16)0.f;
       }
-      qf[cc] = v;
+      qf[qh][kk] = v;
     }
   }
-  uint32_t offA[NDB], offB[NDB];
-  vt_offsets<D>(lane, offA, offB);
-  uint32_t koff[NC];
-  k_offsets<D>(lane, koff);
+  // LDS byte offsets: K operand of key half kh, k-step kk (row kh*16 + c, col kk*32 + 8g);
+  // V^T reads of dim tile dt (row 4g + c/4, col dt*16 + 4 (c % 4)); rows 16 further sit
+  // 32*D bytes further, rows 32 further 64*D (the swizzle uses row bits 0..3)
+  uint32_t kof[2][NK];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) kof[kh][kk] = 2u * (uint32_t)tile_off<D>(kh * 16 + c16, kk * 32 + 8 * g4);
+  uint32_t vof[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+    vof[dt] = 2u * (uint32_t)tile_off<D>(4 * g4 + (c16 >> 2), dt * 16 + 4 * (c16 & 3));
   const uint32_t lds0 = lds_addr(lds_b);
 
-  f32x16 o[NDB];
+  f32x4 o[NDT][2];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = zero16();
-  float ms = kNegBig;  // running max in use, in base-2 units (raw max * c)
-  float l = 0.f;       // lane-partial running sum, relative to ms
+  for (int dt = 0; dt < NDT; ++dt) o[dt][0] = o[dt][1] = zero4();
+  float ms[2] = {kNegBig, kNegBig};  // running max per row, base-2 units
+  float l[2] = {0.f, 0.f};           // lane-partial sums
   const float c = p.c;
+  bool started = false;              // wave-uniform
 
-  // Element mask of the partly allowed blocks of tile t.  The lane's 16 keys are
-  // kr + {0..3, 8..11, 16..19, 24..27}; bit k of `bits` says whether key kr + k is
-  // allowed, so each score takes one bit extract and one bit select.
-  auto mask = [&](int t, const int (&cls)[2], f32x16 (&sc)[2]) {
-    const int src = tsrc(t);
-    const int kt0 = tnum(t) * kBN;
+  // S^T of block kb (tile stage at byte offset KOFF): sc[kh][qh]
+  auto qk = [&](auto koffc, auto kbc, f32x4 (&sc)[2][2]) {
+    constexpr int OFF = decltype(koffc)::value + decltype(kbc)::value * 64 * D;
+    bf16x8 kf[2 * NK];
+    uint32_t a[2 * NK];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (cls[kb] == 1) {
-        const int kr = kt0 + kb * 32 + ((lane >> 5) << 2);
-        const int a = min(max(iv[src].lo - kr, 0), 32);
-        const int e = min(max(iv[src].hi - kr, 0), 32);
-        const uint32_t bits =
-            e <= a ? 0u : (e - a >= 32 ? 0xffffffffu : ((1u << (e - a)) - 1u) << a);
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int off = ((j >> 2) << 3) + (j & 3);
-          const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - off)) >> 31);
-          sc[kb][j] = __uint_as_float((__float_as_uint(sc[kb][j]) & keep) | (~keep & 0xff800000u));
-        }
+      for (int kk = 0; kk < NK; ++kk) a[kh * NK + kk] = lds0 + kof[kh][kk];
+    if constexpr (2 * NK == 8) kread8<OFF>(a, kf);
+    else if constexpr (2 * NK == 4) kread4<OFF>(a, kf);
+    else kread2<OFF>(a, kf);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc = mfma16(kf[kh * NK + kk], qf[qh][kk], acc);
+        sc[kh][qh] = acc;
       }
+  };
+  // mask of a partly allowed block: bit k of bits[qh] (after the lane's shift by 4g)
+  // says whether key k0 + 4g + k of row qr[qh] is allowed
+  auto mask = [&](int t, int kb, f32x4 (&sc)[2][2]) {
+    const int src = tsrc(t);
+    const int k0 = tnum(t) * kBN + kb * 32;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int a = min(max(iv[qh][src].lo - k0, 0), 32);
+      const int e = min(max(iv[qh][src].hi - k0, 0), 32);
+      uint32_t bits = e <= a ? 0u : (e - a >= 32 ? 0xffffffffu : ((1u << (e - a)) - 1u) << a);
+      bits >>= 4 * g4;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int off = kh * 16 + r;
+          const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - off)) >> 31);
+          sc[kh][qh][r] = __uint_as_float((__float_as_uint(sc[kh][qh][r]) & keep) | (~keep & 0xff800000u));
+        }
     }
   };
-  // Numerators of one 32-key block against the running max (online softmax, base 2),
-  // packed to bf16, their lane sum added to l.  Rescaling is lazy and needs no row max
-  // on the common path: when a lane's sum exceeds kBound (the row's first keys, or
-  // scores that outgrew the running max), the row takes its max over the block,
-  // rescales O and l, and the block's numerators are formed again.  The decision is
-  // per row (the lane pair), so a row's arithmetic depends on its own keys only.  Each
-  // block's P^T is accumulated right after its numerators, so one block's P is live.
-  // The wave's first block starts from O = 0 and l = 0: each row takes its max over
-  // the block at once (rows with no allowed key there keep the "no key yet" max).
-  bool started = false;  // wave-uniform
-  auto block_softmax = [&](const f32x16& sblk, bf16x8 (&pbk)[2]) {
+  // numerators of row half qh against its running max: 8 values, packed (key order
+  // 4g + r, then 16 + 4g + r), lane sum returned
+  auto expq = [&](const f32x4 (&sc)[2][2], int qh, bf16x8& pb) {
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    const float nm = -ms[qh];
+    float e[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      e[r] = fast_exp2(fmaf(sc[0][qh][r], c, nm));
+      e[4 + r] = fast_exp2(fmaf(sc[1][qh][r], c, nm));
+    }
+    pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x2 pr = {pb[2 * k], pb[2 * k + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+    return acc;
+  };
+  auto row_max = [&](const f32x4 (&sc)[2][2], int qh) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fmaxf(sc[0][qh][r], sc[1][qh][r]));
+    return quad_max(mx);
+  };
+  // online softmax of one block (lazy rescale as in train_fwd_bf16_kernel, per row)
+  auto softmax = [&](const f32x4 (&sc)[2][2], bf16x8 (&pb)[2]) {
     if (!started) {
       started = true;
-      float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sblk[j]);
-      const float rmax = pair_max(mx);
-      if (rmax > -INFINITY) ms = rmax * c;
-      l = exp_pack(sblk, c, -ms, pbk, 0.f);
+      for (int qh = 0; qh < 2; ++qh) {
+        const float rmax = row_max(sc, qh);
+        if (rmax > -INFINITY) ms[qh] = rmax * c;
+        l[qh] = expq(sc, qh, pb[qh]);
+      }
       return;
     }
-    float rs = exp_pack(sblk, c, -ms, pbk, 0.f);
-    if (__builtin_amdgcn_ballot_w64(rs > kBound) != 0) {
-      float mx = -INFINITY;
+    float rs[2];
+    rs[0] = expq(sc, 0, pb[0]);
+    rs[1] = expq(sc, 1, pb[1]);
+    if (__builtin_amdgcn_ballot_w64(rs[0] > kBound || rs[1] > kBound) != 0) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sblk[j]);
-      const float rmax = pair_max(mx);
-      const bool need = pair_max(rs > kBound ? 1.f : 0.f) > 0.f;
-      if (need) {
-        const float m_new = rmax * c;
-        const float alpha = fast_exp2(ms - m_new);
-        l *= alpha;
+      for (int qh = 0; qh < 2; ++qh) {
+        const float rmax = row_max(sc, qh);
+        const bool need = quad_max(rs[qh] > kBound ? 1.f : 0.f) > 0.f;
+        if (need) {
+          const float m_new = rmax * c;
+          const float alpha = fast_exp2(ms[qh] - m_new);
+          l[qh] *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-        ms = m_new;
+            for (int r = 0; r < 4; ++r) o[dt][qh][r] *= alpha;
+          ms[qh] = m_new;
+        }
+        rs[qh] = expq(sc, qh, pb[qh]);
       }
-      rs = exp_pack(sblk, c, -ms, pbk, 0.f);
     }
-    l += rs;
+    l[0] += rs[0];
+    l[1] += rs[1];
   };
+  // O^T += V^T P^T for block kb (V tile at byte offset VOFF)
+  auto pv = [&](auto voffc, auto kbc, const bf16x8 (&pb)[2]) {
+    constexpr int OFF = decltype(voffc)::value + decltype(kbc)::value * 64 * D;
+    uint32_t a[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) a[dt] = lds0 + vof[dt];
+    long lo[NDT], hi[NDT];
+    tr_reads1<OFF>(a, lo);
+    tr_reads1<OFF + 32 * D>(a, hi);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x8 vt = join_bf16(lo[dt], hi[dt]);
+      o[dt][0] = mfma16(vt, pb[0], o[dt][0]);
+      o[dt][1] = mfma16(vt, pb[1], o[dt][1]);
+    }
+  };
+
   {
-    // ---- one tile at a time through a kStages-deep ring: tiles t+1 .. t+kStages-1 are
-    //      in flight while tile t is computed.  Unrolled by kStages so the stage of each
-    //      tile is a constant that the LDS reads carry in their offset field.  Tiles
-    //      [0, nf) are full for every row of the workgroup (keys of blocks before the
-    //      first row's block) and skip classification and masks.
-    static_assert(kStages >= 2 && kStages <= 4, "unrolled for 2..4 stages");
     const Interval cm = common_interval(kind, 0, q0, r_last, S, L, 0);
     const int nf = max(0, min(min(cm.hi / kBN, tr0.last) - tr0.first, n0));
     auto tile = [&](int t, auto stg) {
       constexpr int KOFF = decltype(stg)::value * STAGE * 2;
       constexpr int VOFF = KOFF + TILE * 2;
-      // Tile t must have landed; the tiles issued after it (up to kStages - 2 of them)
-      // may stay in flight.  The barrier then makes every wave's part of tile t visible
-      // and frees the stage of tile t-1 for tile t+kStages-1.
-      if constexpr (kStages >= 4) {
-        if (t + 2 < ntot) wait_vmem<2 * NIW>();
-        else if (t + 1 < ntot) wait_vmem<NIW>();
-        else wait_vmem<0>();
-      } else if constexpr (kStages == 3) {
-        if (t + 1 < ntot) wait_vmem<NIW>();
-        else wait_vmem<0>();
-      } else {
-        wait_vmem<0>();
-      }
+      wait_vmem<0>();
       __syncthreads();
-      if (t + kStages - 1 < ntot) issue(t + kStages - 1);
+      if (t + 1 < ntot) issue(t + 1);
       int cls[2];
       if (t < nf) {
         cls[0] = cls[1] = wave_live ? 2 : 0;
       } else {
         classify_tile(t, cls);
       }
-      const int want = (cls[0] ? 1 : 0) | (cls[1] ? 2 : 0);
-      if (!want) return;
-      f32x16 sc[2];
-      qk_blocks<D, 2, KOFF>(lds0, koff, qf, sc, want);
-      if (t >= nf) mask(t, cls, sc);
       if (cls[0]) {
+        f32x4 sc[2][2];
+        qk(IntC<KOFF>{}, IntC<0>{}, sc);
+        if (cls[0] == 1) mask(t, 0, sc);
         bf16x8 pb[2];
-        block_softmax(sc[0], pb);
-        pv_block<D, VOFF>(lds0, offA, offB, pb, o);
+        softmax(sc, pb);
+        pv(IntC<VOFF>{}, IntC<0>{}, pb);
       }
       if (cls[1]) {
+        f32x4 sc[2][2];
+        qk(IntC<KOFF>{}, IntC<1>{}, sc);
+        if (cls[1] == 1) mask(t, 1, sc);
         bf16x8 pb[2];
-        block_softmax(sc[1], pb);
-        pv_block<D, VOFF + 64 * D>(lds0, offA, offB, pb, o);
+        softmax(sc, pb);
+        pv(IntC<VOFF>{}, IntC<1>{}, pb);
       }
     };
-    for (int t = 0; t < ntot; t += kStages) {
+    for (int t = 0; t < ntot; t += 2) {
       tile(t, IntC<0>{});
       if (t + 1 < ntot) tile(t + 1, IntC<1>{});
-      if constexpr (kStages > 2) {
-        if (t + 2 < ntot) tile(t + 2, IntC<2 % kStages>{});
-      }
-      if constexpr (kStages > 3) {
-        if (t + 3 < ntot) tile(t + 3, IntC<3 % kStages>{});
-      }
     }
   }
 
-  // ---- epilogue
-  const float l_tot = pair_sum(l);
-  if (row_ok) {
-    const float inv = 1.f / l_tot;
-    __bf16* orow = p.o[slot] + q_off + (size_t)qi * D;
+  // ---- epilogue: O = O^T / l (lane: dims dt*16 + 4g .. +3 of row qr[qh]), LSE
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int qh = 0; qh < 2; ++qh) {
+    const float l_tot = quad_sum(l[qh]);
+    if (rok[qh]) {
+      const float inv = 1.f / l_tot;
+      __bf16* orow = p.o[slot] + q_off + (size_t)qr[qh] * D + 4 * g4;
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = db * 32 + jg * 8 + ((lane >> 5) << 2);
+      for (int dt = 0; dt < NDT; ++dt) {
         bf16x4 v;
-        v[0] = (__bf16)(o[db][jg * 4 + 0] * inv);
-        v[1] = (__bf16)(o[db][jg * 4 + 1] * inv);
-        v[2] = (__bf16)(o[db][jg * 4 + 2] * inv);
-        v[3] = (__bf16)(o[db][jg * 4 + 3] * inv);
-        *(bf16x4*)(orow + d) = v;
+        v[0] = (__bf16)(o[dt][qh][0] * inv);
+        v[1] = (__bf16)(o[dt][qh][1] * inv);
+        v[2] = (__bf16)(o[dt][qh][2] * inv);
+        v[3] = (__bf16)(o[dt][qh][3] * inv);
+        *(bf16x4*)(orow + dt * 16) = v;
       }
-    if (p.lse[slot] != nullptr && lane < 32)
-      p.lse[slot][((size_t)b * p.Hq + hq) * p.L + qi] =
-          (ms + __log2f(l_tot)) * 0.6931471805599453f;
+      if (p.lse[slot] != nullptr && g4 == 0)
+        p.lse[slot][((size_t)b * p.Hq + hq) * p.L + qr[qh]] = (ms[qh] + __log2f(l_tot)) * 0.6931471805599453f;
+    }
   }
   if (p.visits != nullptr && threadIdx.x == 0) atomicAdd(p.visits, (unsigned long long)ntot);
 }
