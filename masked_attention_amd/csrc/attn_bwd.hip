@@ -15,10 +15,12 @@
 //   1. dQ: query-stationary, the forward's schedule: a workgroup owns 128 query rows
 //      of one (batch, query head, kind) and walks the key tiles holding an allowed
 //      pair.  It first forms delta_i = <do_i, o_i> and lse_i * log2(e) of its rows
-//      (fp32, also written to the workspace for launch 2).  Per 32x32 block: S^T =
-//      K Q^T and dP^T = V dO^T on the MFMA (K and V rows from LDS, Q and dO in
-//      registers), P^T = 2^(S^T c - lse), dS^T = P^T (dP^T - delta), then dQ^T += K^T
-//      dS^T with K^T from the transposing LDS read.
+//      (fp32, also written to the workspace for launch 2).  Per 32x32 block, as four
+//      16x16 tiles of v_mfma_f32_16x16x32_bf16 (the forward's layout): S^T = K Q^T and
+//      dP^T = V dO^T (K and V rows from LDS, Q and dO in registers), P^T = 2^(S^T c -
+//      lse), dS^T = P^T (dP^T - delta), then dQ^T += K^T dS^T with K^T from the
+//      transposing LDS read.  (The dK/dV kernel stays on 32x32x16: at one wave per
+//      SIMD, d = 128, the 16x16 form measured 4.06 against 3.90 ms for the backward.)
 //   2. dK/dV: key-stationary: a workgroup owns 128 keys of one (batch, kv head, key
 //      source) and walks the 64-row query tiles that allow any of them -- every query
 //      head of the group, and for the clean keys both the encoder's and the decoder's
@@ -111,17 +113,25 @@ __global__ __launch_bounds__(256, D > 64 ? 2 : 3) void bwd_dq_kernel(BwdParams p
   };
   if (ntot > 0) issue(0);
 
-  // per-wave rows and per-lane query row
+  // per-wave rows; lane l (c = l % 16, g = l / 16) serves the query rows wq0 + c and
+  // wq0 + 16 + c, and in a 32-key block the keys 4g + r and 16 + 4g + r (r < 4), as the
+  // 16x16 tiles of v_mfma_f32_16x16x32_bf16 lay them out (see attn_train.hip)
+  const int c16 = lane & 15, g4 = lane >> 4;
   const int wq0 = q0 + wave * 32;
   const bool wave_live = wq0 < L;
   const int wr1 = min(wq0 + 32, L) - 1;
-  const int qi = wq0 + (lane & 31);
-  const bool row_ok = qi < L;
-  Interval iv[2];
+  int qr[2];
+  bool rok[2];
+  Interval iv[2][2];
 #pragma unroll
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    iv[sidx] = row_interval(kind, sidx, row_ok ? qi : 0, S, L, 0);
-    if (!row_ok) iv[sidx] = Interval{0, 0};
+  for (int qh = 0; qh < 2; ++qh) {
+    qr[qh] = wq0 + qh * 16 + c16;
+    rok[qh] = qr[qh] < L;
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      iv[qh][sidx] = row_interval(kind, sidx, rok[qh] ? qr[qh] : 0, S, L, 0);
+      if (!rok[qh]) iv[qh][sidx] = Interval{0, 0};
+    }
   }
   Interval wu[2] = {{0, 0}, {0, 0}}, wc[2] = {{0, 0}, {0, 0}};
   if (wave_live) {
@@ -149,94 +159,141 @@ __global__ __launch_bounds__(256, D > 64 ? 2 : 3) void bwd_dq_kernel(BwdParams p
     }
   };
 
-  // Q and dO rows of this lane's query as S^T / dP^T operands; lse and delta
-  const size_t q_row = ((size_t)b * p.Hq + hq) * (size_t)L + (row_ok ? qi : 0);
-  bf16x8 qf[NC], df[NC];
-  {
-    const __bf16* qrow = (slot ? p.q[1] : p.q[0]) + q_row * D + ((lane >> 5) << 3);
-    const __bf16* drow = (slot ? p.dO[1] : p.dO[0]) + q_row * D + ((lane >> 5) << 3);
+  // Q and dO of the lane's rows as S^T / dP^T operands (dims kk*32 + 8g .. +7); lse
+  // and delta per row
+  constexpr int NK = D / 32, NDT = D / 16;
+  const size_t row_base = ((size_t)b * p.Hq + hq) * (size_t)L;
+  bf16x8 qf[2][NK], df[2][NK];
+  float dlt[2], lse2[2];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      qf[cc] = *(const bf16x8*)(qrow + cc * 16);
-      df[cc] = *(const bf16x8*)(drow + cc * 16);
-    }
-  }
-  // delta = <dO, O> of this lane's row (the pair of lanes l, l^32 holds it in halves),
-  // and lse * log2(e); both also go to the workspace for the dK/dV kernel.  Rows past
-  // L: lse = +inf makes every p zero.
-  float dlt, lse2;
-  {
-    const __bf16* orow = (slot ? p.o[1] : p.o[0]) + q_row * D + ((lane >> 5) << 3);
+  for (int qh = 0; qh < 2; ++qh) {
+    const size_t q_row = row_base + (rok[qh] ? qr[qh] : 0);
+    const __bf16* qrow = (slot ? p.q[1] : p.q[0]) + q_row * D + (g4 << 3);
+    const __bf16* drow = (slot ? p.dO[1] : p.dO[0]) + q_row * D + (g4 << 3);
+    const __bf16* orow = (slot ? p.o[1] : p.o[0]) + q_row * D + (g4 << 3);
     float part = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const bf16x8 ov = *(const bf16x8*)(orow + cc * 16);
+    for (int kk = 0; kk < NK; ++kk) {
+      qf[qh][kk] = *(const bf16x8*)(qrow + kk * 32);
+      df[qh][kk] = *(const bf16x8*)(drow + kk * 32);
+      const bf16x8 ov = *(const bf16x8*)(orow + kk * 32);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) part = fmaf((float)ov[j], (float)df[cc][j], part);
+      for (int j = 0; j < 8; ++j) part = fmaf((float)ov[j], (float)df[qh][kk][j], part);
     }
-    dlt = pair_sum(part);
-    lse2 = (slot ? p.lse[1] : p.lse[0])[q_row] * kLog2e;
-    if (row_ok && lane < 32) {
-      (slot ? p.delta[1] : p.delta[0])[q_row] = dlt;
-      (slot ? p.lse2[1] : p.lse2[0])[q_row] = lse2;
+    // delta = <dO, O> of the row (its four lanes hold quarters) and lse * log2(e); both
+    // also go to the workspace for the dK/dV kernel.  Rows past L: lse = +inf makes
+    // every p zero.
+    dlt[qh] = quad_sum(part);
+    lse2[qh] = (slot ? p.lse[1] : p.lse[0])[q_row] * kLog2e;
+    if (rok[qh] && g4 == 0) {
+      (slot ? p.delta[1] : p.delta[0])[q_row] = dlt[qh];
+      (slot ? p.lse2[1] : p.lse2[0])[q_row] = lse2[qh];
     }
-    if (!row_ok) {
-      dlt = 0.f;
-      lse2 = INFINITY;
+    if (!rok[qh]) {
+      dlt[qh] = 0.f;
+      lse2[qh] = INFINITY;
     }
   }
-  uint32_t koff[NC];
-  k_offsets<D>(lane, koff);
-  uint32_t offA[NDB], offB[NDB];
-  vt_offsets<D>(lane, offA, offB);
+  // LDS byte offsets: K/V operand rows kh*16 + c, cols kk*32 + 8g; K^T reads of dim tile
+  // dt (row 4g + c/4, col dt*16 + 4 (c % 4)); rows 16 further sit 32*D bytes further
+  uint32_t kof[2 * NK];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) kof[kh * NK + kk] = 2u * (uint32_t)tile_off<D>(kh * 16 + c16, kk * 32 + 8 * g4);
+  uint32_t tof[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+    tof[dt] = 2u * (uint32_t)tile_off<D>(4 * g4 + (c16 >> 2), dt * 16 + 4 * (c16 & 3));
   const uint32_t lds0 = lds_addr(lds_b);
   const float c = p.c;
 
-  f32x16 dq[NDB];
+  f32x4 dq[NDT][2];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+  for (int dt = 0; dt < NDT; ++dt) dq[dt][0] = dq[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // 2 NK operand rows of a 32-key block at LDS byte offset OFF
+  auto rows = [&](auto offc, bf16x8 (&f)[2 * NK]) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(offc)::value;
+    uint32_t a[2 * NK];
+#pragma unroll
+    for (int i = 0; i < 2 * NK; ++i) a[i] = lds0 + kof[i];
+    if constexpr (2 * NK == 8) kread8<OFF>(a, f);
+    else if constexpr (2 * NK == 4) kread4<OFF>(a, f);
+    else kread2<OFF>(a, f);
+  };
   // one 32-key block kb of the tile in stage STG
-  auto block = [&](int t, int kb, int cl, auto stg) __attribute__((always_inline)) {
-    constexpr int KOFF = decltype(stg)::value * STAGE * 2;
-    bf16x8 kf[NC];
-    if (kb == 0) kread_block<D, 0, KOFF>(lds0, koff, kf);
-    else kread_block<D, 1, KOFF>(lds0, koff, kf);
-    f32x16 st = zero16();
+  auto block = [&](int t, auto kbc, int cl, auto stg) __attribute__((always_inline)) {
+    constexpr int KOFF = decltype(stg)::value * STAGE * 2 + decltype(kbc)::value * 64 * D;
+    constexpr int VOFF = KOFF + TILE * 2;
+    f32x4 st[2][2], dpt[2][2];
+    {
+      bf16x8 kf[2 * NK];
+      rows(IntC<KOFF>{}, kf);
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) st = mfma32(kf[cc], qf[cc], st);
-    if (kb == 0) kread_block<D, 0, KOFF + TILE * 2>(lds0, koff, kf);
-    else kread_block<D, 1, KOFF + TILE * 2>(lds0, koff, kf);
-    f32x16 dpt = zero16();
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) dpt = mfma32(kf[cc], df[cc], dpt);
+        for (int qh = 0; qh < 2; ++qh) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) acc = mfma16(kf[kh * NK + kk], qf[qh][kk], acc);
+          st[kh][qh] = acc;
+        }
+      rows(IntC<VOFF>{}, kf);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) acc = mfma16(kf[kh * NK + kk], df[qh][kk], acc);
+          dpt[kh][qh] = acc;
+        }
+    }
     if (cl == 1) {
-      const Interval r = tsrc(t) ? iv[1] : iv[0];
-      const int kr = tnum(t) * kTK + kb * 32 + ((lane >> 5) << 2);
+      const int src = tsrc(t);
+      const int k0 = tnum(t) * kTK + decltype(kbc)::value * 32;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = kr + ((j >> 2) << 3) + (j & 3);
-        if (key < r.lo || key >= r.hi) st[j] = -INFINITY;
+      for (int qh = 0; qh < 2; ++qh) {
+        const int a = min(max(iv[qh][src].lo - k0, 0), 32);
+        const int e = min(max(iv[qh][src].hi - k0, 0), 32);
+        uint32_t bits = e <= a ? 0u : (e - a >= 32 ? 0xffffffffu : ((1u << (e - a)) - 1u) << a);
+        bits >>= 4 * g4;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - (kh * 16 + r))) >> 31);
+            st[kh][qh][r] = __uint_as_float((__float_as_uint(st[kh][qh][r]) & keep) | (~keep & 0xff800000u));
+          }
       }
     }
     bf16x8 dsb[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int qh = 0; qh < 2; ++qh) {
       float e[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pj = fast_exp2(fmaf(st[8 * h + j], c, -lse2));
-        e[j] = pj * (dpt[8 * h + j] - dlt);
-      }
-      dsb[h] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pj = fast_exp2(fmaf(st[kh][qh][r], c, -lse2[qh]));
+          e[kh * 4 + r] = pj * (dpt[kh][qh][r] - dlt[qh]);
+        }
+      dsb[qh] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
-    bf16x8 kt[2][NDB];
-    if (kb == 0) read_vt_tile32<D, KOFF>(lds0, offA, offB, kt);
-    else read_vt_tile32<D, KOFF + 64 * D>(lds0, offA, offB, kt);
+    // dQ^T += K^T dS^T: K^T of the block's keys in the lane order 4g + r, 16 + 4g + r
+    uint32_t a[NDT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int dt = 0; dt < NDT; ++dt) a[dt] = lds0 + tof[dt];
+    long lo[NDT], hi[NDT];
+    tr_reads1<KOFF>(a, lo);
+    tr_reads1<KOFF + 32 * D>(a, hi);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(kt[h][db], dsb[h], dq[db]);
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x8 kt = join_bf16(lo[dt], hi[dt]);
+      dq[dt][0] = mfma16(kt, dsb[0], dq[dt][0]);
+      dq[dt][1] = mfma16(kt, dsb[1], dq[dt][1]);
+    }
   };
   auto tile = [&](int t, auto stg) __attribute__((always_inline)) {
     wait_vmem<0>();   // tile t is the only load in flight
@@ -244,29 +301,28 @@ __global__ __launch_bounds__(256, D > 64 ? 2 : 3) void bwd_dq_kernel(BwdParams p
     if (t + 1 < ntot) issue(t + 1);
     int cls[2];
     classify_tile(t, cls);
-    if (cls[0]) block(t, 0, cls[0], stg);
-    if (cls[1]) block(t, 1, cls[1], stg);
+    if (cls[0]) block(t, IntC<0>{}, cls[0], stg);
+    if (cls[1]) block(t, IntC<1>{}, cls[1], stg);
   };
   for (int t = 0; t < ntot; t += 2) {
     tile(t, IntC<0>{});
     if (t + 1 < ntot) tile(t + 1, IntC<1>{});
   }
 
-  // dQ = scale * dQ^T, rows of this lane's query
-  if (row_ok) {
-    __bf16* out = (slot ? p.dq[1] : p.dq[0]) + q_row * D;
+  // dQ = scale * dQ^T: the lane holds dims dt*16 + 4g .. +3 of its two rows
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int qh = 0; qh < 2; ++qh) {
+    if (!rok[qh]) continue;
+    __bf16* out = (slot ? p.dq[1] : p.dq[0]) + (row_base + qr[qh]) * D + 4 * g4;
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = db * 32 + jg * 8 + ((lane >> 5) << 2);
-        bf16x4 v;
-        v[0] = (__bf16)(dq[db][jg * 4 + 0] * p.scale);
-        v[1] = (__bf16)(dq[db][jg * 4 + 1] * p.scale);
-        v[2] = (__bf16)(dq[db][jg * 4 + 2] * p.scale);
-        v[3] = (__bf16)(dq[db][jg * 4 + 3] * p.scale);
-        *(bf16x4*)(out + d) = v;
-      }
+    for (int dt = 0; dt < NDT; ++dt) {
+      bf16x4 v;
+      v[0] = (__bf16)(dq[dt][qh][0] * p.scale);
+      v[1] = (__bf16)(dq[dt][qh][1] * p.scale);
+      v[2] = (__bf16)(dq[dt][qh][2] * p.scale);
+      v[3] = (__bf16)(dq[dt][qh][3] * p.scale);
+      *(bf16x4*)(out + dt * 16) = v;
+    }
   }
 }
 

@@ -85,24 +85,6 @@ struct Geo {
 //   O^T tile (dt, qh) += V^T[dt*16 .. +16][keys] P^T[keys][qh*16 .. +16] over the
 //     block's 32 keys in the lane order 4g + r, 16 + 4g + r: B = the lane's 8
 //     numerators of row qh*16 + c, A = V^T (lane: dim dt*16 + c, the same 8 keys).
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// max / sum over the four lanes c + 16 g of one query row (v_permlane32_swap, then
-// v_permlane16_swap: every lane gets its group's values in lane order, checked on gfx950)
-__device__ __forceinline__ float quad_max(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 template <int D>
 __global__ __launch_bounds__(LoopCfg<D>::kThreads, LoopCfg<D>::kBlocksPerCU) void train_fwd_bf16_kernel(TrainParams p) {

@@ -59,6 +59,30 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// v_mfma_f32_16x16x32_bf16, C[16x16] += A[16x32] * B[32x16] (checked on gfx950):
+//   A: lane l holds A[l % 16][8*(l/16) .. 8*(l/16)+7]
+//   B: lane l holds B[8*(l/16) .. 8*(l/16)+7][l % 16]
+//   C: lane l, register r holds C[4*(l/16) + r][l % 16]
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Max / sum over the four lanes l % 16 + 16 g (g = 0..3), which hold one row of the
+// 16x16 layout: v_permlane32_swap, then v_permlane16_swap; every lane gets its group's
+// values in lane order (checked on gfx950), so all four compute the same result.
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
 // Wave-uniform value (moves it to a scalar register).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
