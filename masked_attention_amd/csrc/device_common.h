@@ -45,18 +45,13 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Max / sum of x over the lane pair (l, l ^ 32), which hold the two halves of one query
-// row in the 32x32 accumulator layout.  v_permlane32_swap gives every lane the values
+// Max of x over the lane pair (l, l ^ 32), which hold the two halves of one query row in
+// the 32x32 accumulator layout.  v_permlane32_swap gives every lane the values
 // of lanes l % 32 and l % 32 + 32 (checked on gfx950), combined in that fixed order.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // v_mfma_f32_16x16x32_bf16, C[16x16] += A[16x32] * B[32x16] (checked on gfx950):
@@ -137,31 +132,6 @@ __device__ __forceinline__ int tile_off(int r, int col) {
   return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
 }
 
-// Direct global->LDS load of rows [row0, row0 + ROWS) of a [n_rows][D] bf16 matrix
-// into a swizzled LDS tile.  Rows at or past n_rows read row n_rows - 1 instead (their
-// scores are masked off; their values stay finite).  The calling waves split the
-// 16-byte slots: wave w issues instructions w, w + n_waves, ...; each instruction
-// fills 64 consecutive slots (1 KiB).  `tile` and the wave index must be uniform.
-template <int D, int ROWS>
-__device__ __forceinline__ void load_tile_lds(const __bf16* __restrict__ src, int row0,
-                                              int n_rows, __bf16 E2D2_LDS* tile, int wave,
-                                              int n_waves, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int NI = ROWS * CH / 64;
-  static_assert(ROWS * CH % 64 == 0, "tile must be a whole number of 1 KiB slices");
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (i % n_waves != wave) continue;
-    const int slot = i * 64 + lane;
-    const int r = slot / CH;
-    const int pc = slot % CH;
-    const int lc = pc ^ swz<D>(r);
-    int g = row0 + r;
-    g = g < n_rows ? g : n_rows - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)g * D + lc * 8),
-                                     (E2D2_LDS void*)(tile + i * 512), 16, 0, 0);
-  }
-}
 
 // Buffer resource over `bytes` bytes at `base` (raw, unswizzled, 32-bit records).  Loads
 // past `bytes` return zero.
@@ -211,40 +181,8 @@ __device__ __forceinline__ void k_offsets(int lane, uint32_t (&koff)[D / 16]) {
     koff[cc] = 2u * (uint32_t)tile_off<D>(lane & 31, cc * 16 + ((lane >> 5) << 3));
 }
 
-// MFMA A-operand read of K for S^T = K Q^T: lane l gets K[row0 + l%32][col0 + 8*(l/32) ..+7].
-template <int D>
-__device__ __forceinline__ bf16x8 read_k_frag(const __bf16 E2D2_LDS* tile, int row0, int col0,
-                                              int lane) {
-  const int r = row0 + (lane & 31);
-  const int col = col0 + ((lane >> 5) << 3);
-  return *(const bf16x8 E2D2_LDS*)(tile + tile_off<D>(r, col));
-}
 
-// MFMA A-operand read of V^T for O^T += V^T P^T, for the 16 keys [key0, key0 + 16)
-// and the 32 head dims [d0, d0 + 32): lane l gets V[k][d0 + l%32] for the eight keys
-// k = key0 + 4*(l/32) + {0,1,2,3} and key0 + 8 + 4*(l/32) + {0,1,2,3}, which is the
-// key order of the P^T operand taken from the S^T accumulator.
-template <int D>
-__device__ __forceinline__ bf16x8 read_vt_frag(const __bf16 E2D2_LDS* tile, int key0, int d0,
-                                               int lane) {
-  const int g = lane >> 5;
-  const int s = lane & 15;
-  const int col = d0 + (((lane >> 4) & 1) << 4) + ((s & 3) << 2);
-  const int r_a = key0 + (g << 2) + (s >> 2);
-  const int r_b = r_a + 8;
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (i16x4 E2D2_LDS*)(tile + tile_off<D>(r_a, col)));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (i16x4 E2D2_LDS*)(tile + tile_off<D>(r_b, col)));
-  // Whole-vector reinterpretation (element-wise casts of the 16-bit lanes were
-  // mis-assembled into the MFMA operand by the compiler).
-  const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
-  const bf16x4 bb = __builtin_bit_cast(bf16x4, b);
-  const bf16x8 out = __builtin_shufflevector(ab, bb, 0, 1, 2, 3, 4, 5, 6, 7);
-  return out;
-}
 
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
@@ -406,21 +344,6 @@ __device__ __forceinline__ void kread2(const uint32_t (&a)[2], bf16x8 (&o)[2]) {
       : "memory");
 }
 
-// Part of a 32-row block's operands: o[i] = the 16 bytes kread_block would put in
-// kf[C0 + i], for i < CN (CN in {2, 4, 8}); lets a caller hold half the operands.
-template <int D, int KB, int BASE, int C0, int CN>
-__device__ __forceinline__ void kread_part(uint32_t kbase, const uint32_t (&koff)[D / 16],
-                                           bf16x8 (&o)[CN]) {
-  constexpr int OFF = BASE + KB * 64 * D;
-  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field is 16 bits");
-  static_assert(C0 + CN <= D / 16, "operand range");
-  uint32_t a[CN];
-#pragma unroll
-  for (int i = 0; i < CN; ++i) a[i] = kbase + koff[C0 + i];
-  if constexpr (CN == 8) kread8<OFF>(a, o);
-  else if constexpr (CN == 4) kread4<OFF>(a, o);
-  else kread2<OFF>(a, o);
-}
 
 // S^T = K Q^T for the 32-key blocks of a K tile at LDS byte address kbase whose mask
 // `want` is set (bit kb = block kb; NB blocks of 32 keys, 64*D bytes apart).  The K
@@ -472,7 +395,9 @@ __device__ __forceinline__ bf16x8 join_bf16(long lo, long hi) {
 // Per-lane byte offsets, inside a swizzled V tile, of the two transposing reads that
 // give lane l its V^T operand for keys [0, 16) and head dims [32*db, 32*db + 32); the
 // operands of keys [16j, 16j + 16) sit 32*D*j bytes further (rows 16 apart share the
-// swizzle).  See read_vt_frag for the key order.
+// swizzle).  Lane l receives V[k][32*db + l%32] for the eight keys k = 4*(l/32) +
+// {0,1,2,3} and 8 + 4*(l/32) + {0,1,2,3} of the 16, the key order of the P^T operand
+// taken from the 32x32 S^T accumulator.
 template <int D>
 __device__ __forceinline__ void vt_offsets(int lane, uint32_t (&offA)[D / 32],
                                            uint32_t (&offB)[D / 32]) {
@@ -487,38 +412,6 @@ __device__ __forceinline__ void vt_offsets(int lane, uint32_t (&offA)[D / 32],
   }
 }
 
-// V^T operands of a whole 64-key tile at LDS byte address vbase: vf[j][db] covers keys
-// [16j, 16j + 16) and head dims [32 db, 32 db + 32).
-template <int D, int BASE = 0>
-__device__ __forceinline__ void read_vt_tile64(uint32_t vbase, const uint32_t (&offA)[D / 32],
-                                               const uint32_t (&offB)[D / 32],
-                                               bf16x8 (&vf)[4][D / 32]) {
-  constexpr int NDB = D / 32;
-  constexpr int OFF = 32 * D;  // 16 rows
-  if constexpr (NDB == 1) {
-    const uint32_t a[4] = {vbase + offA[0], vbase + offA[0] + 2 * OFF, vbase + offB[0],
-                           vbase + offB[0] + 2 * OFF};
-    long o[8];
-    tr_reads<BASE, BASE + OFF>(a, o);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vf[j][0] = join_bf16(o[j], o[4 + j]);
-  } else {
-#pragma unroll
-    for (int dp = 0; dp < NDB; dp += 2) {
-      const uint32_t a[8] = {vbase + offA[dp], vbase + offA[dp] + 2 * OFF, vbase + offB[dp],
-                             vbase + offB[dp] + 2 * OFF, vbase + offA[dp + 1],
-                             vbase + offA[dp + 1] + 2 * OFF, vbase + offB[dp + 1],
-                             vbase + offB[dp + 1] + 2 * OFF};
-      long o[16];
-      tr_reads<BASE, BASE + OFF>(a, o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vf[j][dp] = join_bf16(o[j], o[4 + j]);
-        vf[j][dp + 1] = join_bf16(o[8 + j], o[12 + j]);
-      }
-    }
-  }
-}
 
 // V^T operands of a 32-key tile: vf[j][db] covers keys [16j, 16j + 16), j = 0, 1.
 template <int D, int BASE = 0>
@@ -576,25 +469,6 @@ struct IntC {
   static constexpr int value = N;
 };
 
-// One 16-row half h of read_vt_tile32's operands: vf[db] == read_vt_tile32's vf[h][db].
-template <int D, int BASE, int H>
-__device__ __forceinline__ void read_vt_half32(uint32_t vbase, const uint32_t (&offA)[D / 32],
-                                               const uint32_t (&offB)[D / 32],
-                                               bf16x8 (&vf)[D / 32]) {
-  constexpr int NDB = D / 32;
-  constexpr int O = BASE + H * 32 * D;
-  static_assert(O >= 0 && O < 65536, "LDS offset field is 16 bits");
-  uint32_t a[2 * NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    a[2 * db] = vbase + offA[db];
-    a[2 * db + 1] = vbase + offB[db];
-  }
-  long o[2 * NDB];
-  tr_reads1<O>(a, o);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) vf[db] = join_bf16(o[2 * db], o[2 * db + 1]);
-}
 
 // LDS byte address of an LDS pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void E2D2_LDS* p) {
@@ -675,7 +549,8 @@ __device__ __forceinline__ long lds_read_tr(const char E2D2_LDS* base, uint32_t 
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 E2D2_LDS*)(base + off + OFF));
   return __builtin_bit_cast(long, v);
 }
-// read_vt_half32 with compiler-scheduled reads.
+// V^T operands of one 16-key half H of a 32-key block (vt_offsets' key order) with
+// compiler-scheduled reads: vf[db] covers head dims [32*db, 32*db + 32).
 template <int D, int BASE, int H>
 __device__ __forceinline__ void read_vt_half32_lds(const char E2D2_LDS* base,
                                                    const uint32_t (&offA)[D / 32],
