@@ -457,6 +457,8 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
       ccm[n] = col_common(kind, src, kw0, kw1 - 1, S, L);
     }
   }
+  // the K / V registers have landed before the loop, so no wait for them sits inside it
+  drain_vmem_visible();
   uint32_t koff[NC];
   k_offsets<D>(lane, koff);
   uint32_t offA[NDB], offB[NDB];
@@ -470,69 +472,122 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
     dv[db] = zero16();
   }
 
-  // rows of a 32-row block (KB) of the tile at LDS offset BASE, times the registers w:
-  // the S = Q K^T (or dP = dO V^T) block.  The LDS reads of this kernel are left to
-  // the compiler (its loads are issued from asm, see TileDma), which overlaps them
-  // with the MFMAs: at one or two waves per SIMD nothing else hides their latency.
+  // Per 32-row query block the work runs in three phases, fenced so the compiler keeps
+  // their order:
+  //   A  S = Q K^T and dP = dO V^T (Q, dO rows as A operands, K and V in registers),
+  //      with this block's transposed operands (dO^T, Q^T) and row statistics (lse,
+  //      delta) read from LDS in between the products;
+  //   B  P = 2^(S c - lse) and dS = P (dP - delta), packed to bf16 (VALU only);
+  //   C  dV^T += dO^T P and dK^T += Q^T dS, with the Q / dO rows of the tile's next
+  //      block read in between.
+  // At one or two waves per SIMD nothing else hides LDS latency, so every read is
+  // issued a whole phase before its first use instead of one product before it.
   const char E2D2_LDS* ldsc = (const char E2D2_LDS*)smem_raw;
-  auto rows_dot = [&](auto kbc, auto basec, const bf16x8 (&w)[NC]) __attribute__((always_inline)) {
-    constexpr int KB = decltype(kbc)::value, BASE = decltype(basec)::value;
-    constexpr int OFF = BASE + KB * 64 * D;
-    f32x16 acc = zero16();
+  constexpr int NDS_A = 8 + 8 * NDB;  // LDS reads of phase A: lse, delta, dO^T, Q^T
+  // Q and dO rows of query block QB of the tile in stage STG
+  auto load_rows = [&](auto qbc, auto stg, bf16x8 (&qr)[NC], bf16x8 (&dr)[NC])
+      __attribute__((always_inline)) {
+    constexpr int QOFF = decltype(stg)::value * STAGE_B + decltype(qbc)::value * 64 * D;
+    constexpr int DOFF = QOFF + TILE * 2;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) acc = mfma32(lds_read16<OFF>(ldsc, koff[cc]), w[cc], acc);
-    return acc;
+    for (int cc = 0; cc < NC; ++cc) {
+      qr[cc] = lds_read16<QOFF>(ldsc, koff[cc]);
+      dr[cc] = lds_read16<DOFF>(ldsc, koff[cc]);
+    }
   };
-  // query block qb (32 rows) of the tile in stage STG, stream slot ss, query tile qt
-  auto block = [&](auto qbc, int cl, int ss, int qt, auto stg) __attribute__((always_inline)) {
+  // query block QB of the tile in stage STG (stream slot ss, query tile qt); qr / dr hold
+  // its rows; with NEXT, the rows of block QB + 1 are read into them in phase C
+  auto block = [&](auto qbc, int cl, int ss, int qt, auto stg, bf16x8 (&qr)[NC],
+                   bf16x8 (&dr)[NC], auto nextc) __attribute__((always_inline)) {
     constexpr int QB = decltype(qbc)::value;
-    constexpr int QOFF = decltype(stg)::value * STAGE_B;
+    constexpr int STG = decltype(stg)::value;
+    constexpr bool NEXT = decltype(nextc)::value;
+    constexpr int QOFF = STG * STAGE_B;
     constexpr int DOFF = QOFF + TILE * 2;
     constexpr int SOFF = QOFF + 2 * TILE * 2;
-    f32x16 s = rows_dot(IntC<QB>{}, IntC<QOFF>{}, kf);
-    const f32x16 dp = rows_dot(IntC<QB>{}, IntC<DOFF>{}, vf);
     // this lane's 16 query rows: QB * 32 + 8 (j / 4) + 4 (lane / 32) + j % 4
     const float E2D2_LDS* lse_t = (const float E2D2_LDS*)(smem_raw + SOFF);
     const float E2D2_LDS* dlt_t = lse_t + 64;
     const int rb = QB * 32 + ((lane >> 5) << 2);
+
+    // ---- phase A
+    f32x4 lq[4], dq4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lq[i] = *(const f32x4 E2D2_LDS*)(lse_t + rb + 8 * i);
+      dq4[i] = *(const f32x4 E2D2_LDS*)(dlt_t + rb + 8 * i);
+    }
+    bf16x8 tdo[2][NDB], tq[2][NDB];
+    read_vt_half32_lds<D, DOFF + QB * 64 * D, 0>(ldsc, offA, offB, tdo[0]);
+    read_vt_half32_lds<D, QOFF + QB * 64 * D, 0>(ldsc, offA, offB, tq[0]);
+    read_vt_half32_lds<D, DOFF + QB * 64 * D, 1>(ldsc, offA, offB, tdo[1]);
+    read_vt_half32_lds<D, QOFF + QB * 64 * D, 1>(ldsc, offA, offB, tq[1]);
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      s = mfma32(qr[cc], kf[cc], s);
+      dp = mfma32(dr[cc], vf[cc], dp);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NC; ++i) {
+      constexpr int PER = NDS_A / (2 * NC), EXTRA = NDS_A % (2 * NC);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product, then its share of reads
+      if (i < EXTRA) __builtin_amdgcn_sched_group_barrier(0x100, PER + 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase B
     if (cl == 1) {
+      // rows [r.lo, r.hi) allow this lane's key: a 32-bit row mask of the block, shifted
+      // to the lane's row set; register j holds block row 8 (j / 4) + j % 4 of that set
       const Interval r = ss ? civ[1] : civ[0];
-      const int q_r = qt * kTK + rb;
+      const int r0 = qt * kTK + QB * 32;
+      const int a = min(max(r.lo - r0, 0), 32);
+      const int e = min(max(r.hi - r0, 0), 32);
+      uint32_t bits = e <= a ? 0u : (e - a >= 32 ? 0xffffffffu : ((1u << (e - a)) - 1u) << a);
+      bits >>= (lane >> 5) << 2;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int q = q_r + ((j >> 2) << 3) + (j & 3);
-        if (q < r.lo || q >= r.hi) s[j] = -INFINITY;
+        const int off = ((j >> 2) << 3) + (j & 3);
+        const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - off)) >> 31);
+        s[j] = __uint_as_float((__float_as_uint(s[j]) & keep) | (~keep & 0xff800000u));
       }
     }
-    // per 16-row half h: P and dS of registers 8h .. 8h+7, then dV^T += dO^T P and
-    // dK^T += Q^T dS for those 16 query rows
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const f32x4 l0 = *(const f32x4 E2D2_LDS*)(lse_t + rb + 16 * h);
-      const f32x4 l1 = *(const f32x4 E2D2_LDS*)(lse_t + rb + 16 * h + 8);
-      const f32x4 d0 = *(const f32x4 E2D2_LDS*)(dlt_t + rb + 16 * h);
-      const f32x4 d1 = *(const f32x4 E2D2_LDS*)(dlt_t + rb + 16 * h + 8);
       float e[8], f[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float lj = j < 4 ? l0[j] : l1[j - 4];
-        const float dj = j < 4 ? d0[j] : d1[j - 4];
+        const float lj = lq[2 * h + (j >> 2)][j & 3];
+        const float dj = dq4[2 * h + (j >> 2)][j & 3];
         const float pj = fast_exp2(fmaf(s[8 * h + j], c, -lj));
         e[j] = pj;
         f[j] = pj * (dp[8 * h + j] - dj);
       }
-      const bf16x8 pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      const bf16x8 dsb = to_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
-      bf16x8 tf[NDB];
-      if (h == 0) read_vt_half32_lds<D, DOFF + QB * 64 * D, 0>(ldsc, offA, offB, tf);
-      else read_vt_half32_lds<D, DOFF + QB * 64 * D, 1>(ldsc, offA, offB, tf);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) dv[db] = mfma32(tf[db], pb, dv[db]);
-      if (h == 0) read_vt_half32_lds<D, QOFF + QB * 64 * D, 0>(ldsc, offA, offB, tf);
-      else read_vt_half32_lds<D, QOFF + QB * 64 * D, 1>(ldsc, offA, offB, tf);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) dk[db] = mfma32(tf[db], dsb, dk[db]);
+      pb[h] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      dsb[h] = to_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase C
+    if constexpr (NEXT) load_rows(IntC<QB + 1>{}, stg, qr, dr);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = mfma32(tdo[h][db], pb[h], dv[db]);
+        dk[db] = mfma32(tq[h][db], dsb[h], dk[db]);
+      }
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int i = 0; i < 4 * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto tile = [&](int u, auto stg) __attribute__((always_inline)) {
     wait_vmem<0>();   // tile u is the only load in flight
@@ -543,6 +598,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
     locate(u, ss, hq, qt);
     const Interval un = ss ? cu[1] : cu[0];
     const Interval cm = ss ? ccm[1] : ccm[0];
+    int cls[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int r0 = qt * kTK + qb * 32;
@@ -551,10 +607,20 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void bwd_dkv_kernel(BwdParams 
       if (r1 <= un.lo || r0 >= un.hi || r1 <= r0) cl = 0;
       else if (cm.lo <= r0 && r1 <= cm.hi && r1 - r0 == 32 && kw1 - kw0 == 32) cl = 2;
       else cl = 1;
-      if (cl) {
-        if (qb == 0) block(IntC<0>{}, cl, ss, qt, stg);
-        else block(IntC<1>{}, cl, ss, qt, stg);
+      cls[qb] = cl;
+    }
+    bf16x8 qr[NC], dr[NC];
+    if (cls[0]) {
+      load_rows(IntC<0>{}, stg, qr, dr);
+      if (cls[1]) {
+        block(IntC<0>{}, cls[0], ss, qt, stg, qr, dr, BoolC<true>{});
+        block(IntC<1>{}, cls[1], ss, qt, stg, qr, dr, BoolC<false>{});
+      } else {
+        block(IntC<0>{}, cls[0], ss, qt, stg, qr, dr, BoolC<false>{});
       }
+    } else if (cls[1]) {
+      load_rows(IntC<1>{}, stg, qr, dr);
+      block(IntC<1>{}, cls[1], ss, qt, stg, qr, dr, BoolC<false>{});
     }
   };
   for (int u = 0; u < ntot; u += 2) {
