@@ -37,6 +37,20 @@
 namespace e2d2 {
 namespace {
 
+// Wait for every outstanding vector-memory operation, as an instruction the compiler's
+// wait-count pass sees (vmcnt 0; expcnt and lgkmcnt left at their maxima, 7 and 15).
+// Needed after registers are loaded in a kernel's prologue when the main loop issues
+// its LDS-DMA loads from asm: without it the pass still counts the prologue loads as
+// outstanding inside the loop and places vmcnt waits at their first uses there, which
+// the hardware then applies to the loop's own in-flight prefetch.
+__device__ __forceinline__ void drain_vmem_visible() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// A compile-time bool carried as a value.
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 constexpr int kTK = 64;     // keys per K/V tile (dQ) and query rows per Q/dO tile (dK/dV)
 constexpr int kRows = 128;  // query rows (dQ) or keys (dK/dV) per workgroup: 4 waves x 32
 constexpr int kWaves = 4;

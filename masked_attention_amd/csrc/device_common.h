@@ -182,19 +182,13 @@ __device__ __forceinline__ void k_offsets(int lane, uint32_t (&koff)[D / 16]) {
 }
 
 
+
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-
-// Wait for every outstanding vector-memory operation, as an instruction the compiler's
-// wait-count pass sees (vmcnt 0; expcnt and lgkmcnt left at their maxima, 7 and 15).
-// Needed after registers are loaded in a kernel's prologue when the main loop issues
-// its LDS-DMA loads from asm: without it the pass still counts the prologue loads as
-// outstanding inside the loop and places vmcnt waits at their first uses there, which
-// the hardware then applies to the loop's own in-flight prefetch.
-__device__ __forceinline__ void drain_vmem_visible() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------------
 // Transposing LDS reads of V in one asm block that also waits for them.  Written as
@@ -473,10 +467,6 @@ __device__ __forceinline__ void pv_block(uint32_t vbase, const uint32_t (&offA)[
 template <int N>
 struct IntC {
   static constexpr int value = N;
-};
-template <bool B>
-struct BoolC {
-  static constexpr bool value = B;
 };
 
 
