@@ -24,9 +24,11 @@
 //   2. dK/dV: key-stationary: a workgroup owns 128 keys of one (batch, kv head, key
 //      source) and walks the 64-row query tiles that allow any of them -- every query
 //      head of the group, and for the clean keys both the encoder's and the decoder's
-//      queries -- so each key's gradient is summed in one place.  Per 32x32 block:
-//      S = Q K^T and dP = dO V^T (Q, dO rows from LDS, K and V in registers), then
-//      dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from the transposing read.
+//      queries -- so each key's gradient is summed in one place.  Per 32x32 block, in
+//      three phases fenced against the scheduler (described at the block loop):
+//      S = Q K^T and dP = dO V^T (Q, dO rows from LDS, K and V in registers), then P
+//      and dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from the
+//      transposing read.
 //   Query and key tiles are staged through a 2-deep LDS ring with buffer_load ... lds,
 //   as in the forward; partial 32x32 blocks are masked per element from the closed-
 //   form row / column intervals (schedule.h), empty ones are skipped.
