@@ -20,7 +20,9 @@
 // v_mfma_f32_32x32x16_bf16 with W rows as the A operand.  The k axis is walked 64 at
 // a time through an ST-deep ring of swizzled LDS stages (the swizzle of the attention
 // K tiles) filled straight from memory by buffer_load_dwordx4 ... lds; ST - 1 stages
-// are in flight while one is multiplied.  The loads are issued from inline asm and
+// are in flight while one is multiplied.  A step issues its refill halfway through its
+// products (measured on MI355X: 2.8% off the decoder-layer step against issuing it
+// right after the barrier).  The loads are issued from inline asm and
 // their completion is waited for explicitly (s_waitcnt vmcnt) before a bare
 // s_barrier: the compiler then neither drains every prefetch at the barrier nor
 // before each LDS read, and it schedules the plain C++ LDS reads of the operands
@@ -156,7 +158,6 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void linear_bf16_kernel(
     // stage kt landed; the stages issued after it (up to ST - 2) may still be in flight
     wait_groups<NL>(min(ST - 2, nk - 1 - kt));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + ST - 1 < nk) issue(kt + ST - 1, IntC<(decltype(stg)::value + ST - 1) % ST>{});
     constexpr int SL = decltype(stg)::value;
     const char E2D2_LDS* stb = lds_b + SL * STAGE;
     bf16x8 wf[NBW][4], af[MBW][4];
@@ -170,11 +171,20 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void linear_bf16_kernel(
         af[mb][cc] = *(const bf16x8 E2D2_LDS*)(stb + aofs + mb * 4096 + koff[cc]);
     }
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+    for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[nb][mb] = mfma32(wf[nb][cc], af[mb][cc], acc[nb][mb]);
+      if (cc == 1) {
+        // Refill the slot read in the previous step (every wave left it before the
+        // barrier above) once half of this step's products are issued: issued right
+        // after the barrier, the loads of all waves delay the first products.
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + ST - 1 < nk) issue(kt + ST - 1, IntC<(SL + ST - 1) % ST>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
   for (int kt = 0; kt < nk; kt += ST) {
     step(kt, IntC<0>{});
