@@ -21,7 +21,7 @@
 // a time through an ST-deep ring of swizzled LDS stages (the swizzle of the attention
 // K tiles) filled straight from memory by buffer_load_dwordx4 ... lds; ST - 1 stages
 // are in flight while one is multiplied.  A step issues its refill halfway through its
-// products (measured on MI355X: 2.8% off the decoder-layer step against issuing it
+// products (measured on MI355X: 2.1% off the decoder-layer step against issuing it
 // right after the barrier).  The loads are issued from inline asm and
 // their completion is waited for explicitly (s_waitcnt vmcnt) before a bare
 // s_barrier: the compiler then neither drains every prefetch at the barrier nor
