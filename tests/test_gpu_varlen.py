@@ -4,12 +4,14 @@ applied sequence by sequence.  Tolerances as in test_gpu_train.py; appends bitwi
 """
 import sys
 
+import numpy as np
 import pytest
 import torch
 
 import masked_attention_amd as m
 import oracle
-from helpers import TensorKind as K, check, counter, host, scale_of
+from helpers import TensorKind as K, check, counter, gpu_fill, host, scale_of
+from synth import host_tensor, tensor_id
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +65,45 @@ def _varlen_case(B, Hq, Hkv, S, d, lens, max_len, cap, seed):
             check(lse[b, h], rl[0, h], "bf16", f"lse[{b},{h}] C={C}")
         visits += m.e2d2_attn_count_tiles(m.KIND_DENOISE, 1, Hq, 0, S, C, 32, 32)[0]
     assert int(vis.item()) == visits
+
+
+def test_varlen_full_size_bench_lengths():
+    # The per-sequence-length workload as timed: B32 Hq16/Hkv8 d128, block 32, cache
+    # capacity 2048 + 32, lengths drawn from [1024, 2048] with the same seeded generator,
+    # inputs filled on the GPU.  Every query head of four sequences (the shortest, the
+    # longest and two others) is checked against the oracle; the tile-visit counter
+    # against the host schedule summed over all 32 sequences.
+    B, Hq, Hkv, d, S, max_len = 32, 16, 8, 128, 32, 2048
+    cap = max_len + S
+    seed = 0xE2D20009
+    lens = np.random.RandomState(seed & 0xFFFFFFFF).randint(1024, max_len + 1, size=B)
+    say(f"[varlen full] B{B} Hq{Hq} Hkv{Hkv} d{d} S{S} lens {int(lens.min())}..{int(lens.max())}")
+    kc = gpu_fill((B, Hkv, cap, d), seed, K.K_CACHE, "bf16", rows=max_len)
+    vc = gpu_fill((B, Hkv, cap, d), seed, K.V_CACHE, "bf16", rows=max_len)
+    q = gpu_fill((B, Hq, S, d), seed, K.Q_BLK, "bf16", step=0)
+    kb = gpu_fill((B, Hkv, S, d), seed, K.K_BLK, "bf16", step=0)
+    vb = gpu_fill((B, Hkv, S, d), seed, K.V_BLK, "bf16", step=0)
+    o = torch.full((B, Hq, S, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq, S), float("nan"), device="cuda")
+    vis = counter()
+    m.e2d2_attn_denoise_step_varlen(q, kc, vc, torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                    max_len, kb, vb, o, lse_blk=lse,
+                                    workspace=_workspace(B, Hq, Hkv, S, d, max_len), tile_visits=vis)
+    torch.cuda.synchronize()
+    want = sum(m.e2d2_attn_count_tiles(m.KIND_DENOISE, 1, Hq, 0, S, int(C), 32, 32)[0] for C in lens)
+    assert int(vis.item()) == want
+    picks = sorted({int(lens.argmin()), int(lens.argmax()), 7, 20})
+    for b in picks:
+        C = int(lens[b])
+        qh = host_tensor(seed, tensor_id(K.Q_BLK, 0), (1, Hq, S, d), "bf16", b0=b)
+        kch = host_tensor(seed, tensor_id(K.K_CACHE), (1, Hkv, C, d), "bf16", b0=b)
+        vch = host_tensor(seed, tensor_id(K.V_CACHE), (1, Hkv, C, d), "bf16", b0=b)
+        kbh = host_tensor(seed, tensor_id(K.K_BLK, 0), (1, Hkv, S, d), "bf16", b0=b)
+        vbh = host_tensor(seed, tensor_id(K.V_BLK, 0), (1, Hkv, S, d), "bf16", b0=b)
+        ro, rl = oracle.denoise_step(qh, kch, vch, C, kbh, vbh, scale_of(d))
+        for h in range(Hq):
+            check(o[b, h], ro[0, h], "bf16", f"o[{b},{h}] C={C}")
+            check(lse[b, h], rl[0, h], "bf16", f"lse[{b},{h}] C={C}")
 
 
 def test_varlen_with_equal_lengths_is_the_uniform_step_bitwise():
