@@ -119,6 +119,23 @@ def test_training_attention_full_size():
     _train_case(8, 16, 16, 1024, 16, 64, "bf16", 0xE2D20002, heads=heads)
 
 
+def test_layer_calls_equal_combined_launch_full_size():
+    # The per-layer calls the layer-split benchmark times, at the training workload's size:
+    # the encoder-only call and the decoder-only launch are bitwise the combined launch's
+    # encoder and decoder outputs on every head (the combined launch is checked against
+    # the oracle here on one head and on a spread of heads in the full-size test above).
+    B, Hq, Hkv, L, S, d = 8, 16, 16, 1024, 16, 64
+    r = _train_case(B, Hq, Hkv, L, S, d, "bf16", 0xE2D20002, heads=[(5, 11)])
+    g = r["g"]
+    oe, od = torch.empty_like(r["oe"]), torch.empty_like(r["od"])
+    le, ld = torch.empty_like(r["le"]), torch.empty_like(r["ld"])
+    m.e2d2_attn_encoder_blockcausal(g["qe"], g["kc"], g["vc"], oe, S, lse=le)
+    m.e2d2_attn_train_fwd(g["qd"], g["kc"], g["vc"], g["kd"], g["vd"], od, S, lse_dec=ld)
+    torch.cuda.synchronize()
+    assert torch.equal(oe, r["oe"]) and torch.equal(le, r["le"])
+    assert torch.equal(od, r["od"]) and torch.equal(ld, r["ld"])
+
+
 def test_long_sequence_full_size_sampled_rows():
     # B2 Hq16 Hkv8 d128 L8192 S64 bf16: sampled rows of sampled heads.
     rows = np.unique(np.concatenate([np.arange(0, 70), np.arange(8100, 8192),
