@@ -495,10 +495,9 @@ def bench_decoder_layer(steps_per_block, reps, seed):
         torch.matmul(o2, w_o.t(), out=y2)
 
     def lib_gemms_around_attention():
-        # The library products in the layer's order, with the attention between them:
-        # its 268 MB cache stream evicts the weights from the Infinity Cache, as it does
-        # for the layer's own projections.  Minus the attention alone, this is the cost
-        # the library products would have inside the layer step.
+        # The library products in the layer's order with the attention between them, as
+        # in the layer step.  Minus the attention alone, this is what they would cost
+        # inside the step, measured the way projections_us measures the layer's own.
         torch.matmul(x2, w_qkv.t(), out=qkv2)
         attn_step()
         torch.matmul(o2, w_o.t(), out=y2)
